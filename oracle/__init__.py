@@ -1,0 +1,212 @@
+"""CPU oracle for the sigmoid group-limited MoE gate and its dispatch.
+
+TEST INFRASTRUCTURE ONLY.  This package is the float64 checker that the HIP
+library is compared against.  Only ``tests/``, ``__graft_entry__.smoke()`` and
+the ``cpu_baseline`` leg of ``bench.py`` may import it.  It shares no code with
+the HIP library (``sigmoid_group_limited_amd``) and imports nothing from it.
+
+The arithmetic lives in ``oracle.c`` (plain loops, float64, OpenMP over
+tokens); this module only compiles it with gcc and marshals numpy arrays.
+
+Sources the steps follow (page title, then the part of the page):
+  * DeepSeek-V3.2-Exp · Normalize weights -- the "Code" excerpt (Gate forward)
+    and the equation for G_i;
+  * Kimi K2 · Normalize weights -- the "Code" excerpt (gate forward) and the
+    equation for G_i;
+  * AI Engineer Exhaustive · DeepSeek-V3 MoE Router -- "How it works"
+    (eq. for s_{i,t}, eq. for g'_{i,t} and g_{i,t}, the bias and the
+    node-limited routing paragraphs, the route_scale paragraph);
+  * Kimi K2 · Add shared output -- the "Code" excerpt, first lines of
+    moe_infer (counts, argsort, row gather).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from dataclasses import dataclass
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+SOURCE = os.path.join(_HERE, "oracle.c")
+LIBRARY = os.path.join(_HERE, "liboracle.so")
+
+OK = 0
+EINVAL = -1
+
+
+def compile_oracle(source: str = SOURCE, output: str = LIBRARY,
+                   strict: bool = True) -> str:
+    """Compile ``source`` into a shared library at ``output`` with gcc
+    (warnings are errors when ``strict``)."""
+    cmd = ["gcc", "-O2", "-fopenmp", "-shared", "-fPIC", "-std=c99", "-Wall"]
+    cmd += ["-Werror"] if strict else []
+    cmd += [source, "-o", output + ".tmp", "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(output + ".tmp", output)
+    return output
+
+
+def _needs_build(output: str, source: str) -> bool:
+    return (not os.path.exists(output)
+            or os.path.getmtime(output) < os.path.getmtime(source))
+
+
+@dataclass
+class GateResult:
+    weights: np.ndarray   # float64 [T, K]
+    indices: np.ndarray   # int32   [T, K]
+    margins: np.ndarray   # float64 [T, 2]: (v_K - v_K+1, gs_KG - gs_KG+1)
+
+
+@dataclass
+class DispatchResult:
+    counts: np.ndarray    # int32 [E]
+    offsets: np.ndarray   # int32 [E+1]
+    perm: np.ndarray      # int32 [T*K]
+
+
+def _ptr(a: np.ndarray, ctype):
+    return a.ctypes.data_as(ctypes.POINTER(ctype))
+
+
+class Oracle:
+    """ctypes view of one compiled copy of ``oracle.c``."""
+
+    def __init__(self, path: str = LIBRARY):
+        self.path = path
+        lib = ctypes.CDLL(path)
+        i64, i32, dbl = ctypes.c_int64, ctypes.c_int, ctypes.c_double
+        P = ctypes.POINTER
+        lib.oracle_num_threads.restype = i32
+        lib.oracle_num_threads.argtypes = []
+        lib.oracle_logits.restype = None
+        lib.oracle_logits.argtypes = [P(ctypes.c_uint16), P(ctypes.c_float),
+                                      i64, i64, i64, P(dbl)]
+        lib.oracle_select.restype = i32
+        lib.oracle_select.argtypes = [P(dbl), P(ctypes.c_float), i64, i64,
+                                      i32, i32, i32, dbl, i32, P(dbl),
+                                      P(ctypes.c_int32), P(dbl)]
+        lib.oracle_gate.restype = i32
+        lib.oracle_gate.argtypes = [P(ctypes.c_uint16), P(ctypes.c_float),
+                                    P(ctypes.c_float), i64, i64, i64, i32,
+                                    i32, i32, dbl, i32, P(dbl),
+                                    P(ctypes.c_int32), P(dbl)]
+        lib.oracle_dispatch.restype = i32
+        lib.oracle_dispatch.argtypes = [P(ctypes.c_int32), i64, i32, i64,
+                                        P(ctypes.c_int32), P(ctypes.c_int32),
+                                        P(ctypes.c_int32)]
+        lib.oracle_gather_rows.restype = i32
+        lib.oracle_gather_rows.argtypes = [P(ctypes.c_uint16), i64, i64, i32,
+                                           P(ctypes.c_int32), i64,
+                                           P(ctypes.c_uint16)]
+        self.lib = lib
+
+    # -- helpers -----------------------------------------------------------
+    def num_threads(self) -> int:
+        return int(self.lib.oracle_num_threads())
+
+    def logits(self, x_bf16: np.ndarray, W: np.ndarray) -> np.ndarray:
+        """float64 logits [T, E] of bfloat16 bits x [T, d] and float32 W [E, d]."""
+        x = np.ascontiguousarray(x_bf16, dtype=np.uint16)
+        W = np.ascontiguousarray(W, dtype=np.float32)
+        T, d = x.shape
+        E, d2 = W.shape
+        if d != d2:
+            raise ValueError("x and W disagree on d")
+        out = np.empty((T, E), dtype=np.float64)
+        self.lib.oracle_logits(_ptr(x, ctypes.c_uint16), _ptr(W, ctypes.c_float),
+                               T, d, E, _ptr(out, ctypes.c_double))
+        return out
+
+    def select(self, logits: np.ndarray, bias: np.ndarray, n_group: int,
+               topk_group: int, top_k: int, route_scale: float,
+               order: int = 0) -> GateResult:
+        """Gate steps after the logits, from float64 logits [T, E]."""
+        L = np.ascontiguousarray(logits, dtype=np.float64)
+        b = np.ascontiguousarray(bias, dtype=np.float32)
+        T, E = L.shape
+        if b.shape != (E,):
+            raise ValueError("bias must have shape [E]")
+        w = np.empty((T, top_k), dtype=np.float64)
+        idx = np.empty((T, top_k), dtype=np.int32)
+        m = np.empty((T, 2), dtype=np.float64)
+        rc = self.lib.oracle_select(_ptr(L, ctypes.c_double), _ptr(b, ctypes.c_float),
+                                    T, E, n_group, topk_group, top_k,
+                                    float(route_scale), order,
+                                    _ptr(w, ctypes.c_double),
+                                    _ptr(idx, ctypes.c_int32),
+                                    _ptr(m, ctypes.c_double))
+        if rc != OK:
+            raise ValueError(f"oracle_select rejected the configuration (rc={rc})")
+        return GateResult(w, idx, m)
+
+    def gate(self, x_bf16: np.ndarray, W: np.ndarray, bias: np.ndarray,
+             n_group: int, topk_group: int, top_k: int, route_scale: float,
+             order: int = 0) -> GateResult:
+        """Whole gate from bfloat16 bits x [T, d], float32 W [E, d], bias [E]."""
+        x = np.ascontiguousarray(x_bf16, dtype=np.uint16)
+        W = np.ascontiguousarray(W, dtype=np.float32)
+        b = np.ascontiguousarray(bias, dtype=np.float32)
+        T, d = x.shape
+        E, d2 = W.shape
+        if d != d2 or b.shape != (E,):
+            raise ValueError("shape mismatch between x, W and bias")
+        w = np.empty((T, top_k), dtype=np.float64)
+        idx = np.empty((T, top_k), dtype=np.int32)
+        m = np.empty((T, 2), dtype=np.float64)
+        rc = self.lib.oracle_gate(_ptr(x, ctypes.c_uint16), _ptr(W, ctypes.c_float),
+                                  _ptr(b, ctypes.c_float), T, d, E, n_group,
+                                  topk_group, top_k, float(route_scale), order,
+                                  _ptr(w, ctypes.c_double),
+                                  _ptr(idx, ctypes.c_int32),
+                                  _ptr(m, ctypes.c_double))
+        if rc != OK:
+            raise ValueError(f"oracle_gate rejected the configuration (rc={rc})")
+        return GateResult(w, idx, m)
+
+    def dispatch(self, indices: np.ndarray, n_experts: int) -> DispatchResult:
+        """Counts, offsets and the stable expert-major permutation."""
+        idx = np.ascontiguousarray(indices, dtype=np.int32)
+        T, K = idx.shape
+        counts = np.empty(n_experts, dtype=np.int32)
+        offsets = np.empty(n_experts + 1, dtype=np.int32)
+        perm = np.empty(T * K, dtype=np.int32)
+        rc = self.lib.oracle_dispatch(_ptr(idx, ctypes.c_int32), T, K, n_experts,
+                                      _ptr(counts, ctypes.c_int32),
+                                      _ptr(offsets, ctypes.c_int32),
+                                      _ptr(perm, ctypes.c_int32))
+        if rc != OK:
+            raise ValueError(f"oracle_dispatch rejected its input (rc={rc})")
+        return DispatchResult(counts, offsets, perm)
+
+    def gather_rows(self, x_bf16: np.ndarray, perm: np.ndarray, top_k: int,
+                    rows: np.ndarray | None = None) -> np.ndarray:
+        """out[pos] = x[perm[pos] // top_k]; ``rows`` picks a subset of pos."""
+        x = np.ascontiguousarray(x_bf16, dtype=np.uint16)
+        T, d = x.shape
+        p = np.ascontiguousarray(perm if rows is None else perm[rows],
+                                 dtype=np.int32)
+        out = np.empty((p.shape[0], d), dtype=np.uint16)
+        rc = self.lib.oracle_gather_rows(_ptr(x, ctypes.c_uint16), T, d, top_k,
+                                         _ptr(p, ctypes.c_int32), p.shape[0],
+                                         _ptr(out, ctypes.c_uint16))
+        if rc != OK:
+            raise ValueError("oracle_gather_rows: permutation entry out of range")
+        return out
+
+
+_DEFAULT: Oracle | None = None
+
+
+def load(rebuild: bool = False) -> Oracle:
+    """The oracle built from ``oracle.c`` next to this file (compiled on
+    first use, or when the source is newer than the library)."""
+    global _DEFAULT
+    if rebuild or _needs_build(LIBRARY, SOURCE):
+        compile_oracle()
+        _DEFAULT = None
+    if _DEFAULT is None:
+        _DEFAULT = Oracle(LIBRARY)
+    return _DEFAULT

@@ -1,0 +1,337 @@
+/*
+ * oracle.c -- plain, slow, float64 CPU definition of the sigmoid
+ * group-limited MoE gate and of its expert-major dispatch.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is the checker that the HIP path is
+ * compared against.  Only the test suite, the smoke check and the CPU-baseline
+ * leg of the benchmark may load it.  It shares no code, header, table or
+ * helper with the HIP library and includes nothing from it.
+ *
+ * Every step is written in the order the pages give it, with no blocking,
+ * fusion or reordering:
+ *
+ *   gate   (DeepSeek-V3.2-Exp · Normalize weights, "Code": Gate forward;
+ *           Kimi K2 · Normalize weights, "Code": gate forward;
+ *           AI Engineer Exhaustive · DeepSeek-V3 MoE Router, "How it works")
+ *     1. logits  L[t,e] = u_t . e_i        (x cast to float, no linear bias)
+ *     2. affinity s = Sigmoid(L)           (eq. for s_{i,t})
+ *     3. choice score v = s + b            (load-balance bias paragraph)
+ *     4. group score = sum of the two largest v in the group
+ *     5. keep the topk_group best groups, all other experts masked to -inf
+ *     6. token top-K over the masked v
+ *     7. gather the UNBIASED s at the winners
+ *     8. renormalise over the K winners, multiply by route_scale
+ *        (eq. for g'/g; Normalize-weights equation G_i)
+ *
+ *   dispatch (Kimi K2 · Add shared output, "Code": moe_infer, first lines)
+ *     per-expert token counts, expert-major argsort of the flat (token, slot)
+ *     pairs, and the row gather x[perm // K].
+ *
+ * Readings taken where the pages leave a choice open:
+ *   - arithmetic is float64 throughout (the pages use float32);
+ *   - masked experts get -inf (DeepSeek-V3.2-Exp page and the study note;
+ *     the Kimi K2 page fills 0.0);
+ *   - every top-k breaks ties towards the LOWER index (experts and groups);
+ *   - order 0 emits a token's K winners in ascending expert id, order 1 in
+ *     selection order (v descending, index ascending);
+ *   - the renormalisation has no epsilon in the denominator;
+ *   - the dispatch permutation is stable: pairs of one expert keep ascending
+ *     flat pair id p = t*K + k.
+ *
+ * Build: gcc -O2 -fopenmp -shared -fPIC oracle.c -o liboracle.so -lm
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORACLE_OK 0
+#define ORACLE_EINVAL (-1)
+
+/* bfloat16 bit pattern -> double.  A bfloat16 is the top half of a float32,
+ * so the conversion is exact. */
+static double bf16_to_double(uint16_t h)
+{
+    uint32_t u = ((uint32_t)h) << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+int oracle_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/* Validate a gate configuration: E experts in G equal groups of S = E/G,
+ * keep KG groups, select K experts among the KG*S candidates. */
+static int check_cfg(int64_t E, int G, int KG, int K)
+{
+    if (E <= 0 || G <= 0 || KG <= 0 || K <= 0) return ORACLE_EINVAL;
+    if (E % G != 0) return ORACLE_EINVAL;
+    if (KG > G) return ORACLE_EINVAL;
+    if (G > 1 && E / G < 2) return ORACLE_EINVAL; /* top-2 of a group needs 2 members */
+    if ((int64_t)K > (int64_t)KG * (E / G)) return ORACLE_EINVAL;
+    return ORACLE_OK;
+}
+
+/* Step 1.  L[t,e] = sum_j x[t,j] * W[e,j] with W laid out [E, d] (expert
+ * rows, as F.linear's weight).  Products of a bfloat16 and a float32 are
+ * exact in double; only the sum rounds. */
+static void logits_row(const uint16_t *x_row, const float *W, int64_t d,
+                       int64_t E, double *L)
+{
+    for (int64_t e = 0; e < E; ++e) {
+        const float *w = W + e * d;
+        double acc = 0.0;
+        for (int64_t j = 0; j < d; ++j)
+            acc += bf16_to_double(x_row[j]) * (double)w[j];
+        L[e] = acc;
+    }
+}
+
+void oracle_logits(const uint16_t *x, const float *W, int64_t T, int64_t d,
+                   int64_t E, double *logits)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t)
+        logits_row(x + t * d, W, d, E, logits + t * E);
+}
+
+/* True when (va, a) comes before (vb, b) in "value descending, index
+ * ascending" order. */
+static int precedes(double va, int64_t a, double vb, int64_t b)
+{
+    if (va > vb) return 1;
+    if (va < vb) return 0;
+    return a < b;
+}
+
+/* Steps 2-8 for one token, from its E logits.
+ *   work: scratch of 3*E + 2*G doubles/ints (caller-provided)
+ *   out_w[K], out_i[K]: weights and expert ids
+ *   margin[2]: {v(K) - v(K+1) among the candidates,
+ *               gs(KG) - gs(KG+1) among the groups}; +inf when undefined. */
+static void select_token(const double *L, const float *bias, int64_t E, int G,
+                         int KG, int K, double route_scale, int order,
+                         double *s, double *v, int *keep, double *gs,
+                         int *chosen, int64_t *sel, double *out_w,
+                         int32_t *out_i, double *margin)
+{
+    const int64_t S = E / G;
+
+    /* Step 2: s = 1 / (1 + exp(-L)). */
+    for (int64_t e = 0; e < E; ++e) s[e] = 1.0 / (1.0 + exp(-L[e]));
+
+    /* Step 3: the bias shifts the choice score only. */
+    for (int64_t e = 0; e < E; ++e) v[e] = s[e] + (double)bias[e];
+
+    /* Steps 4-5: group scores and group keep mask. */
+    for (int g = 0; g < G; ++g) keep[g] = 1;
+    margin[1] = INFINITY;
+    if (G > 1) {
+        for (int g = 0; g < G; ++g) {
+            /* two largest values of the group, counting multiplicity */
+            double top1 = -INFINITY, top2 = -INFINITY;
+            for (int64_t e = g * S; e < (g + 1) * S; ++e) {
+                if (v[e] > top1) {
+                    top2 = top1;
+                    top1 = v[e];
+                } else if (v[e] > top2) {
+                    top2 = v[e];
+                }
+            }
+            gs[g] = top1 + top2;
+        }
+        /* a group is kept when fewer than KG groups precede it */
+        for (int g = 0; g < G; ++g) {
+            int ahead = 0;
+            for (int h = 0; h < G; ++h)
+                if (h != g && precedes(gs[h], h, gs[g], g)) ++ahead;
+            keep[g] = ahead < KG;
+        }
+        if (KG < G) {
+            /* KG-th and (KG+1)-th largest group scores */
+            double kth = -INFINITY, next = -INFINITY;
+            for (int g = 0; g < G; ++g) {
+                int ahead = 0;
+                for (int h = 0; h < G; ++h)
+                    if (h != g && precedes(gs[h], h, gs[g], g)) ++ahead;
+                if (ahead == KG - 1) kth = gs[g];
+                if (ahead == KG) next = gs[g];
+            }
+            margin[1] = kth - next;
+        }
+    }
+
+    /* Step 5 (mask) and step 6: repeatedly take the best remaining
+     * candidate; experts of dropped groups count as -inf and are never
+     * taken because K <= KG*S. */
+    for (int64_t e = 0; e < E; ++e) chosen[e] = 0;
+    for (int k = 0; k < K; ++k) {
+        int64_t best = -1;
+        for (int64_t e = 0; e < E; ++e) {
+            if (!keep[e / S] || chosen[e]) continue;
+            if (best < 0 || precedes(v[e], e, v[best], best)) best = e;
+        }
+        chosen[best] = 1;
+        sel[k] = best;
+    }
+    /* margin between the K-th winner and the best loser among candidates */
+    {
+        double best_loser = -INFINITY;
+        int any = 0;
+        for (int64_t e = 0; e < E; ++e) {
+            if (!keep[e / S] || chosen[e]) continue;
+            if (!any || v[e] > best_loser) best_loser = v[e];
+            any = 1;
+        }
+        margin[0] = any ? v[sel[K - 1]] - best_loser : INFINITY;
+    }
+
+    /* canonical order: ascending expert id */
+    if (order == 0) {
+        for (int a = 1; a < K; ++a) {
+            int64_t key = sel[a];
+            int b = a - 1;
+            while (b >= 0 && sel[b] > key) {
+                sel[b + 1] = sel[b];
+                --b;
+            }
+            sel[b + 1] = key;
+        }
+    }
+
+    /* Steps 7-8: gather unbiased s, renormalise, scale. */
+    double denom = 0.0;
+    for (int k = 0; k < K; ++k) denom += s[sel[k]];
+    for (int k = 0; k < K; ++k) {
+        out_i[k] = (int32_t)sel[k];
+        out_w[k] = s[sel[k]] / denom * route_scale;
+    }
+}
+
+/* Gate from precomputed float64 logits [T, E].
+ *   margins may be NULL; otherwise [T, 2]. */
+int oracle_select(const double *logits, const float *bias, int64_t T,
+                  int64_t E, int G, int KG, int K, double route_scale,
+                  int order, double *weights, int32_t *indices,
+                  double *margins)
+{
+    if (check_cfg(E, G, KG, K) != ORACLE_OK) return ORACLE_EINVAL;
+    if (order != 0 && order != 1) return ORACLE_EINVAL;
+    int failed = 0;
+#pragma omp parallel
+    {
+        double *s = malloc(sizeof(double) * E);
+        double *v = malloc(sizeof(double) * E);
+        double *gs = malloc(sizeof(double) * G);
+        int *keep = malloc(sizeof(int) * G);
+        int *chosen = malloc(sizeof(int) * E);
+        int64_t *sel = malloc(sizeof(int64_t) * K);
+        double mdummy[2];
+        if (!s || !v || !gs || !keep || !chosen || !sel) {
+#pragma omp atomic write
+            failed = 1;
+        } else {
+#pragma omp for schedule(static)
+            for (int64_t t = 0; t < T; ++t)
+                select_token(logits + t * E, bias, E, G, KG, K, route_scale,
+                             order, s, v, keep, gs, chosen, sel,
+                             weights + t * K, indices + t * K,
+                             margins ? margins + 2 * t : mdummy);
+        }
+        free(s); free(v); free(gs); free(keep); free(chosen); free(sel);
+    }
+    return failed ? ORACLE_EINVAL : ORACLE_OK;
+}
+
+/* Whole gate from x (bfloat16 bits, [T, d]), W (float32, [E, d]) and bias
+ * (float32, [E]).  Logits are computed token by token and never stored. */
+int oracle_gate(const uint16_t *x, const float *W, const float *bias,
+                int64_t T, int64_t d, int64_t E, int G, int KG, int K,
+                double route_scale, int order, double *weights,
+                int32_t *indices, double *margins)
+{
+    if (check_cfg(E, G, KG, K) != ORACLE_OK || d <= 0) return ORACLE_EINVAL;
+    if (order != 0 && order != 1) return ORACLE_EINVAL;
+    int failed = 0;
+#pragma omp parallel
+    {
+        double *L = malloc(sizeof(double) * E);
+        double *s = malloc(sizeof(double) * E);
+        double *v = malloc(sizeof(double) * E);
+        double *gs = malloc(sizeof(double) * G);
+        int *keep = malloc(sizeof(int) * G);
+        int *chosen = malloc(sizeof(int) * E);
+        int64_t *sel = malloc(sizeof(int64_t) * K);
+        double mdummy[2];
+        if (!L || !s || !v || !gs || !keep || !chosen || !sel) {
+#pragma omp atomic write
+            failed = 1;
+        } else {
+#pragma omp for schedule(static)
+            for (int64_t t = 0; t < T; ++t) {
+                logits_row(x + t * d, W, d, E, L);
+                select_token(L, bias, E, G, KG, K, route_scale, order, s, v,
+                             keep, gs, chosen, sel, weights + t * K,
+                             indices + t * K,
+                             margins ? margins + 2 * t : mdummy);
+            }
+        }
+        free(L); free(s); free(v); free(gs); free(keep); free(chosen);
+        free(sel);
+    }
+    return failed ? ORACLE_EINVAL : ORACLE_OK;
+}
+
+/* Dispatch metadata from indices [T, K] (flat pair p = t*K + k):
+ *   counts[E]      tokens routed to each expert
+ *   offsets[E+1]   exclusive prefix sum of counts
+ *   perm[T*K]      perm[pos] = p, expert-major, ascending p within an expert
+ * This is a counting sort that walks the pairs in ascending p. */
+int oracle_dispatch(const int32_t *indices, int64_t T, int K, int64_t E,
+                    int32_t *counts, int32_t *offsets, int32_t *perm)
+{
+    const int64_t n = T * (int64_t)K;
+    if (T < 0 || K <= 0 || E <= 0) return ORACLE_EINVAL;
+    for (int64_t p = 0; p < n; ++p)
+        if (indices[p] < 0 || indices[p] >= E) return ORACLE_EINVAL;
+
+    for (int64_t e = 0; e < E; ++e) counts[e] = 0;
+    for (int64_t p = 0; p < n; ++p) counts[indices[p]] += 1;
+
+    offsets[0] = 0;
+    for (int64_t e = 0; e < E; ++e) offsets[e + 1] = offsets[e] + counts[e];
+
+    int32_t *fill = malloc(sizeof(int32_t) * (size_t)E);
+    if (!fill) return ORACLE_EINVAL;
+    for (int64_t e = 0; e < E; ++e) fill[e] = offsets[e];
+    for (int64_t p = 0; p < n; ++p) {
+        int32_t e = indices[p];
+        perm[fill[e]] = (int32_t)p;
+        fill[e] += 1;
+    }
+    free(fill);
+    return ORACLE_OK;
+}
+
+/* Row gather: out[pos, :] = x[perm[pos] / K, :] for pos < n (bfloat16 bits,
+ * rows of d elements). */
+int oracle_gather_rows(const uint16_t *x, int64_t T, int64_t d, int K,
+                       const int32_t *perm, int64_t n, uint16_t *out)
+{
+    for (int64_t pos = 0; pos < n; ++pos) {
+        int64_t p = perm[pos];
+        if (p < 0 || p / K >= T) return ORACLE_EINVAL;
+        memcpy(out + pos * d, x + (p / K) * d, sizeof(uint16_t) * (size_t)d);
+    }
+    return ORACLE_OK;
+}
