@@ -1,0 +1,133 @@
+/*
+ * siggate.h -- C ABI of the MI355X (gfx950) sigmoid group-limited MoE gate
+ * and its expert-major dispatch.
+ *
+ * What the calls compute (sources are page titles and the part of the page):
+ *
+ *   siggate_forward  -- the router of DeepSeek-V3 / Kimi-K2
+ *     (DeepSeek-V3.2-Exp · Normalize weights, "Code": Gate forward;
+ *      Kimi K2 · Normalize weights, "Code": gate forward, and the equation
+ *      for G_i; AI Engineer Exhaustive · DeepSeek-V3 MoE Router,
+ *      "How it works"):
+ *        L = x . W^T in float32 (x upcast from bfloat16, no linear bias),
+ *        s = sigmoid(L), v = s + bias (bias steers the choice only),
+ *        group score = sum of the two largest v of each of n_group groups,
+ *        keep the topk_group best groups, mask the rest to -inf,
+ *        take the top_k experts by v, gather the unbiased s at them,
+ *        w = route_scale * s / sum(s over the top_k).
+ *   siggate_dispatch -- the first lines of moe_infer
+ *     (Kimi K2 · Add shared output, "Code": moe_infer; Kimi K3 · MoE
+ *      update, moe_infer):
+ *        tokens_per_expert = per-expert count of the (token, slot) pairs,
+ *        perm = expert-major order of the flat pair ids p = t*top_k + k,
+ *        permuted_x[pos] = x[perm[pos] / top_k].
+ *
+ * Conventions shared by every call
+ *   - All array arguments are DEVICE pointers owned by the caller; the
+ *     library allocates nothing, keeps no state between calls and is
+ *     reentrant.  Every pointer must be 16-byte aligned.
+ *   - All arrays are dense row-major.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the default
+ *     stream) and runs asynchronously; there is no host synchronisation.
+ *     Argument errors are detected on the host before anything is enqueued
+ *     and leave every output untouched.
+ *   - A selection tie (equal choice scores, or equal group scores) goes to
+ *     the LOWER expert / group index.  The pages leave the tie order open.
+ *   - The dispatch permutation is stable: the pairs of one expert keep
+ *     ascending p, i.e. ascending token id.  The pages use an unstable
+ *     argsort, of which this is one valid result.
+ *   - NaN or Inf in x, W or bias give undefined selections.
+ *
+ * Supported shapes (others return SIGGATE_EUNSUPPORTED):
+ *   E in {128, 256, 384}; n_group a power of two with 1 <= n_group <= 64;
+ *   1 <= top_k <= 8; d a positive multiple of 8; 0 <= T <= 2^31 / top_k.
+ * Invalid configurations return SIGGATE_EINVAL: topk_group outside
+ * [1, n_group], top_k > topk_group * E / n_group, order not 0 or 1.
+ */
+#ifndef SIGGATE_H
+#define SIGGATE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Router hyper-parameters and problem size. */
+typedef struct siggate_cfg {
+    int32_t T;           /* tokens in the batch                               */
+    int32_t d;           /* hidden size (7168 for DeepSeek-V3 and Kimi K2)    */
+    int32_t E;           /* routed experts N_r (256 DeepSeek-V3, 384 Kimi K2) */
+    int32_t n_group;     /* expert groups (8 DeepSeek-V3, 1 Kimi K2)          */
+    int32_t topk_group;  /* groups kept per token (4 DeepSeek-V3, 1 Kimi K2)  */
+    int32_t top_k;       /* experts per token K_r (8 for both)                */
+    float route_scale;   /* 2.5 DeepSeek-V3, 2.827 Kimi K2                    */
+    int32_t order;       /* output order of a token's top_k entries:
+                            0 = ascending expert id,
+                            1 = choice score descending (index ascending on ties) */
+} siggate_cfg_t;
+
+typedef enum siggate_status {
+    SIGGATE_OK = 0,
+    SIGGATE_EINVAL = -1,        /* invalid configuration or null/misaligned pointer */
+    SIGGATE_EUNSUPPORTED = -2,  /* valid configuration this library does not build  */
+    SIGGATE_EWORKSPACE = -3,    /* workspace smaller than siggate_workspace_bytes   */
+    SIGGATE_EHIP = -4           /* the HIP runtime reported a launch error          */
+} siggate_status_t;
+
+/* Bytes of device workspace that siggate_forward and siggate_dispatch need
+ * for this configuration (the larger of the two; 0 is possible).  Returns 0
+ * for a configuration that either call would reject. */
+size_t siggate_workspace_bytes(const siggate_cfg_t *cfg);
+
+/* Gate.
+ *   x        bfloat16 [T, d]  (raw bfloat16 bits)
+ *   W        float32  [E, d]  (router weight, one row per expert)
+ *   bias     float32  [E]     (selection-only bias; required)
+ *   weights  float32  [T, top_k]  out: route_scale * renormalised s
+ *   indices  int32    [T, top_k]  out: selected expert ids
+ *   ws       device workspace of ws_bytes >= siggate_workspace_bytes(cfg)
+ *            (may be NULL when that is 0); its contents on entry do not
+ *            matter and are garbage on return.
+ * Calls that share a workspace must not overlap in time. */
+siggate_status_t siggate_forward(const void *x, const float *W, const float *bias,
+                                 const siggate_cfg_t *cfg, float *weights,
+                                 int32_t *indices, void *ws, size_t ws_bytes,
+                                 void *stream);
+
+/* Dispatch.
+ *   x                  bfloat16 [T, d]
+ *   indices            int32 [T, top_k], every entry in [0, E) and the
+ *                      top_k entries of a token distinct (as the gate makes
+ *                      them); entries out of range are undefined behaviour
+ *   tokens_per_expert  int32 [E]        out
+ *   offsets            int32 [E + 1]    out, exclusive prefix sum of
+ *                      tokens_per_expert (may be NULL)
+ *   perm               int32 [T*top_k]  out, perm[pos] = p
+ *   dest               int32 [T*top_k]  out, dest[p] = pos, the inverse of
+ *                      perm (may be NULL)
+ *   permuted_x         bfloat16 [T*top_k, d] out, row pos = x[perm[pos] / top_k]
+ *   ws                 device workspace (see siggate_forward)
+ * Only T, d, E and top_k of cfg are used. */
+siggate_status_t siggate_dispatch(const void *x, const int32_t *indices,
+                                  const siggate_cfg_t *cfg,
+                                  int32_t *tokens_per_expert, int32_t *offsets,
+                                  int32_t *perm, int32_t *dest, void *permuted_x,
+                                  void *ws, size_t ws_bytes, void *stream);
+
+/* Test hook: the float32 logits L = x . W^T [T, E] that siggate_forward
+ * selects from, computed by the same kernels in the same summation order
+ * (for the same T). */
+siggate_status_t siggate_logits(const void *x, const float *W,
+                                const siggate_cfg_t *cfg, float *logits,
+                                void *ws, size_t ws_bytes, void *stream);
+
+/* Static, human-readable name of a status code. */
+const char *siggate_status_str(siggate_status_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SIGGATE_H */

@@ -1,0 +1,180 @@
+// api.hip -- the C ABI of libsiggate (declared in include/siggate.h):
+// argument checks, workspace layout and kernel launches.  Host code only.
+#include <string.h>
+
+#include "siggate.h"
+#include "siggate_internal.h"
+
+using namespace siggate;
+
+namespace {
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+// Validity first (EINVAL), then what this library builds (EUNSUPPORTED).
+siggate_status_t check_gate_cfg(const siggate_cfg_t *c)
+{
+    if (!c) return SIGGATE_EINVAL;
+    if (c->T < 0 || c->d <= 0 || c->E <= 0 || c->n_group <= 0 || c->top_k <= 0)
+        return SIGGATE_EINVAL;
+    if (c->E % c->n_group != 0) return SIGGATE_EINVAL;
+    if (c->topk_group < 1 || c->topk_group > c->n_group) return SIGGATE_EINVAL;
+    if (c->n_group > 1 && c->E / c->n_group < 2) return SIGGATE_EINVAL;
+    if ((long long)c->top_k > (long long)c->topk_group * (c->E / c->n_group)) return SIGGATE_EINVAL;
+    if (c->order != 0 && c->order != 1) return SIGGATE_EINVAL;
+    if (!(c->route_scale == c->route_scale)) return SIGGATE_EINVAL;   // NaN
+    if (c->E != 128 && c->E != 256 && c->E != 384) return SIGGATE_EUNSUPPORTED;
+    if (c->n_group > 64 || (c->n_group & (c->n_group - 1)) != 0) return SIGGATE_EUNSUPPORTED;
+    if (c->top_k > MAX_TOPK) return SIGGATE_EUNSUPPORTED;
+    if (c->d % 8 != 0) return SIGGATE_EUNSUPPORTED;
+    if ((long long)c->T * c->top_k > 0x7fffffffLL) return SIGGATE_EUNSUPPORTED;
+    return SIGGATE_OK;
+}
+
+siggate_status_t check_dispatch_cfg(const siggate_cfg_t *c)
+{
+    if (!c) return SIGGATE_EINVAL;
+    if (c->T < 0 || c->d <= 0 || c->E <= 0 || c->top_k <= 0) return SIGGATE_EINVAL;
+    if (c->top_k > c->E) return SIGGATE_EINVAL;
+    if (c->E > MAX_EXPERTS || c->top_k > MAX_TOPK || c->d % 8 != 0) return SIGGATE_EUNSUPPORTED;
+    if ((long long)c->T * c->top_k > 0x7fffffffLL) return SIGGATE_EUNSUPPORTED;
+    return SIGGATE_OK;
+}
+
+size_t forward_bytes(const siggate_cfg_t *c)
+{
+    return align256(plan_gate(c->T, c->d, c->E).partial_bytes);
+}
+
+GateArgs gate_args(const void *x, const float *W, const float *bias, const siggate_cfg_t *c,
+                   const GatePlan &p)
+{
+    GateArgs a;
+    memset(&a, 0, sizeof a);
+    a.x = (const uint16_t *)x;
+    a.W = W;
+    a.bias = bias;
+    a.T = c->T;
+    a.d = c->d;
+    a.n_group = c->n_group;
+    a.topk_group = c->topk_group;
+    a.top_k = c->top_k;
+    a.order = c->order;
+    a.route_scale = c->route_scale;
+    a.chunks_total = (c->d + KC - 1) / KC;
+    a.chunks_per_split = p.chunks_per_split;
+    a.n_split = p.n_split;
+    return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t siggate_workspace_bytes(const siggate_cfg_t *cfg)
+{
+    size_t need = 0;
+    if (check_gate_cfg(cfg) == SIGGATE_OK) need = forward_bytes(cfg);
+    if (check_dispatch_cfg(cfg) == SIGGATE_OK) {
+        const size_t db = dispatch_workspace_bytes(cfg->T, cfg->E, cfg->top_k, true);
+        if (db > need) need = db;
+    }
+    return need;
+}
+
+siggate_status_t siggate_forward(const void *x, const float *W, const float *bias,
+                                 const siggate_cfg_t *cfg, float *weights, int32_t *indices,
+                                 void *ws, size_t ws_bytes, void *stream)
+{
+    siggate_status_t st = check_gate_cfg(cfg);
+    if (st != SIGGATE_OK) return st;
+    if (!W || !bias) return SIGGATE_EINVAL;
+    if (cfg->T > 0 && (!x || !weights || !indices)) return SIGGATE_EINVAL;
+    if (!aligned16(x) || !aligned16(W) || !aligned16(bias) || !aligned16(weights) ||
+        !aligned16(indices) || !aligned16(ws))
+        return SIGGATE_EINVAL;
+    const GatePlan p = plan_gate(cfg->T, cfg->d, cfg->E);
+    if (ws_bytes < align256(p.partial_bytes) || (p.partial_bytes && !ws)) return SIGGATE_EWORKSPACE;
+    if (cfg->T == 0) return SIGGATE_OK;
+    GateArgs a = gate_args(x, W, bias, cfg, p);
+    a.weights = weights;
+    a.indices = indices;
+    a.partial = (float *)ws;
+    return launch_gate(a, p, cfg->E, MODE_SELECT, (hipStream_t)stream) == hipSuccess
+               ? SIGGATE_OK
+               : SIGGATE_EHIP;
+}
+
+siggate_status_t siggate_logits(const void *x, const float *W, const siggate_cfg_t *cfg,
+                                float *logits, void *ws, size_t ws_bytes, void *stream)
+{
+    siggate_status_t st = check_gate_cfg(cfg);
+    if (st != SIGGATE_OK) return st;
+    if (!W) return SIGGATE_EINVAL;
+    if (cfg->T > 0 && (!x || !logits)) return SIGGATE_EINVAL;
+    if (!aligned16(x) || !aligned16(W) || !aligned16(logits) || !aligned16(ws))
+        return SIGGATE_EINVAL;
+    const GatePlan p = plan_gate(cfg->T, cfg->d, cfg->E);
+    if (ws_bytes < align256(p.partial_bytes) || (p.partial_bytes && !ws)) return SIGGATE_EWORKSPACE;
+    if (cfg->T == 0) return SIGGATE_OK;
+    GateArgs a = gate_args(x, W, nullptr, cfg, p);
+    a.logits = logits;
+    a.partial = (float *)ws;
+    return launch_gate(a, p, cfg->E, MODE_LOGITS, (hipStream_t)stream) == hipSuccess
+               ? SIGGATE_OK
+               : SIGGATE_EHIP;
+}
+
+siggate_status_t siggate_dispatch(const void *x, const int32_t *indices, const siggate_cfg_t *cfg,
+                                  int32_t *tokens_per_expert, int32_t *offsets, int32_t *perm,
+                                  int32_t *dest, void *permuted_x, void *ws, size_t ws_bytes,
+                                  void *stream)
+{
+    siggate_status_t st = check_dispatch_cfg(cfg);
+    if (st != SIGGATE_OK) return st;
+    if (!tokens_per_expert) return SIGGATE_EINVAL;
+    if (cfg->T > 0 && (!x || !indices || !perm || !permuted_x)) return SIGGATE_EINVAL;
+    if (!aligned16(x) || !aligned16(indices) || !aligned16(tokens_per_expert) ||
+        !aligned16(offsets) || !aligned16(perm) || !aligned16(dest) || !aligned16(permuted_x) ||
+        !aligned16(ws))
+        return SIGGATE_EINVAL;
+    const int T = cfg->T, E = cfg->E, K = cfg->top_k;
+    const size_t need = dispatch_workspace_bytes(T, E, K, dest == nullptr);
+    if (ws_bytes < need || (need && !ws)) return SIGGATE_EWORKSPACE;
+
+    DispatchArgs a;
+    memset(&a, 0, sizeof a);
+    a.x = (const uint16_t *)x;
+    a.indices = indices;
+    a.T = T;
+    a.d = cfg->d;
+    a.E = E;
+    a.top_k = K;
+    a.n_blocks = (T + DISPATCH_BLOCK_TOKENS - 1) / DISPATCH_BLOCK_TOKENS;
+    const size_t cnt_bytes = align256((size_t)a.n_blocks * E * sizeof(int32_t));
+    char *w = (char *)ws;
+    a.block_counts = (int32_t *)w;
+    a.block_base = (int32_t *)(w + cnt_bytes);
+    a.dest = dest ? dest : (int32_t *)(w + 2 * cnt_bytes);
+    a.tokens_per_expert = tokens_per_expert;
+    a.offsets = offsets;
+    a.perm = perm;
+    a.permuted_x = (uint16_t *)permuted_x;
+    return launch_dispatch(a, (hipStream_t)stream) == hipSuccess ? SIGGATE_OK : SIGGATE_EHIP;
+}
+
+const char *siggate_status_str(siggate_status_t status)
+{
+    switch (status) {
+    case SIGGATE_OK: return "SIGGATE_OK: success";
+    case SIGGATE_EINVAL: return "SIGGATE_EINVAL: invalid configuration or null/misaligned pointer";
+    case SIGGATE_EUNSUPPORTED: return "SIGGATE_EUNSUPPORTED: configuration not built by this library";
+    case SIGGATE_EWORKSPACE: return "SIGGATE_EWORKSPACE: workspace smaller than siggate_workspace_bytes";
+    case SIGGATE_EHIP: return "SIGGATE_EHIP: HIP launch error";
+    default: return "unknown siggate status";
+    }
+}
+
+}  // extern "C"

@@ -1,0 +1,208 @@
+// dispatch.hip -- expert-major dispatch of the (token, slot) pairs, for gfx950.
+//
+// What is computed (Kimi K2 · Add shared output, "Code": moe_infer, its
+// first lines; Kimi K3 · MoE update, moe_infer):
+//   tokens_per_expert[e] = #{p : indices_flat[p] == e}
+//   perm = expert-major order of the flat pair ids p = t*K + k, stable
+//          (ascending p inside an expert; the pages' argsort is unstable and
+//          this is one of its valid results)
+//   permuted_x[pos] = x[perm[pos] / K]
+//
+// Four launches, none of them with order-dependent atomics:
+//   count   one block per 256 tokens; each wave ORs a 64-bit lane mask per
+//           expert in LDS (bit l = token l of the wave routes there), so the
+//           block's count of expert e is the popcount of its 4 masks.
+//   scan    one block: per-expert totals, their exclusive prefix (offsets)
+//           and the base position of every (block, expert) run.
+//   scatter recomputes the masks; the rank of a pair inside its block is
+//           the popcount of lower lanes' bits plus earlier waves' counts,
+//           which is exactly ascending token order.
+//   gather  one block per token: read the row once, write it to its K
+//           destinations with non-temporal 16-byte stores.
+#include "siggate_internal.h"
+
+namespace siggate {
+namespace {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int BT = DISPATCH_BLOCK_TOKENS;
+constexpr int WAVES = BT / 64;
+constexpr int SCAN_THREADS = 1024;
+
+// Loads the K expert ids of token t into e[] (-1 past K or for t >= T).
+__device__ __forceinline__ void load_row(const DispatchArgs &a, int t, int (&e)[MAX_TOPK])
+{
+#pragma unroll
+    for (int k = 0; k < MAX_TOPK; ++k) e[k] = -1;
+    if (t >= a.T) return;
+    const int32_t *row = a.indices + (size_t)t * a.top_k;
+    if (a.top_k == 8) {
+        const i32x4 lo = *(const i32x4 *)row;
+        const i32x4 hi = *(const i32x4 *)(row + 4);
+        e[0] = lo[0]; e[1] = lo[1]; e[2] = lo[2]; e[3] = lo[3];
+        e[4] = hi[0]; e[5] = hi[1]; e[6] = hi[2]; e[7] = hi[3];
+    } else {
+#pragma unroll
+        for (int k = 0; k < MAX_TOPK; ++k)
+            if (k < a.top_k) e[k] = row[k];
+    }
+}
+
+// masks[w][e] bit l: token (block, wave w, lane l) has a pair on expert e.
+__device__ __forceinline__ void build_masks(const DispatchArgs &a,
+                                            unsigned long long (*masks)[MAX_EXPERTS],
+                                            const int (&e)[MAX_TOPK], int lane, int wave)
+{
+    for (int i = threadIdx.x; i < WAVES * MAX_EXPERTS; i += BT) (&masks[0][0])[i] = 0ull;
+    __syncthreads();
+    const unsigned long long bit = 1ull << lane;
+#pragma unroll
+    for (int k = 0; k < MAX_TOPK; ++k)
+        if ((unsigned)e[k] < (unsigned)a.E) atomicOr(&masks[wave][e[k]], bit);
+    __syncthreads();
+}
+
+__global__ __launch_bounds__(BT) void dispatch_count_kernel(DispatchArgs a)
+{
+    __shared__ unsigned long long masks[WAVES][MAX_EXPERTS];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int e[MAX_TOPK];
+    load_row(a, blockIdx.x * BT + threadIdx.x, e);
+    build_masks(a, masks, e, lane, wave);
+    for (int x = threadIdx.x; x < a.E; x += BT) {
+        int c = 0;
+#pragma unroll
+        for (int w = 0; w < WAVES; ++w) c += __popcll(masks[w][x]);
+        a.block_counts[(size_t)blockIdx.x * a.E + x] = c;
+    }
+}
+
+__global__ __launch_bounds__(SCAN_THREADS) void dispatch_scan_kernel(DispatchArgs a)
+{
+    __shared__ int seg_sum[SCAN_THREADS];
+    __shared__ int excl[MAX_EXPERTS];
+    __shared__ int wave_tot[SCAN_THREADS / 64];
+    const int E = a.E, NB = a.n_blocks, tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+
+    // Thread (seg, e) sums block_counts[b, e] over its slice of blocks.
+    const int segs = SCAN_THREADS / E;
+    const int seg = tid / E, e = tid - seg * E;
+    const bool active = seg < segs;
+    const int per = (NB + segs - 1) / segs;
+    const int b0 = active ? min(seg * per, NB) : 0;
+    const int b1 = active ? min(b0 + per, NB) : 0;
+    int sum = 0;
+    for (int b = b0; b < b1; ++b) sum += a.block_counts[(size_t)b * E + e];
+    if (active) seg_sum[seg * E + e] = sum;
+    __syncthreads();
+
+    // Per-expert total and its exclusive prefix over experts.
+    int tot = 0;
+    if (tid < E)
+        for (int s = 0; s < segs; ++s) tot += seg_sum[s * E + tid];
+    int inc = tot;
+    for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(inc, off);
+        if (lane >= off) inc += y;
+    }
+    if (lane == 63) wave_tot[wave] = inc;
+    __syncthreads();
+    int ex = inc - tot;
+    for (int w = 0; w < wave; ++w) ex += wave_tot[w];
+    if (tid < E) {
+        excl[tid] = ex;
+        a.tokens_per_expert[tid] = tot;
+        if (a.offsets) a.offsets[tid] = ex;
+        if (tid == E - 1 && a.offsets) a.offsets[E] = ex + tot;
+    }
+    __syncthreads();
+
+    // Base position of the run of (block b, expert e).
+    if (active) {
+        int run = excl[e];
+        for (int s = 0; s < seg; ++s) run += seg_sum[s * E + e];
+        for (int b = b0; b < b1; ++b) {
+            const size_t i = (size_t)b * E + e;
+            const int c = a.block_counts[i];
+            a.block_base[i] = run;
+            run += c;
+        }
+    }
+}
+
+__global__ __launch_bounds__(BT) void dispatch_scatter_kernel(DispatchArgs a)
+{
+    __shared__ unsigned long long masks[WAVES][MAX_EXPERTS];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int t = blockIdx.x * BT + threadIdx.x;
+    int e[MAX_TOPK];
+    load_row(a, t, e);
+    build_masks(a, masks, e, lane, wave);
+    if (t >= a.T) return;
+    const unsigned long long lower = (1ull << lane) - 1ull;
+    const int32_t *base = a.block_base + (size_t)blockIdx.x * a.E;
+#pragma unroll
+    for (int k = 0; k < MAX_TOPK; ++k) {
+        if (k >= a.top_k) break;
+        const size_t p = (size_t)t * a.top_k + k;
+        const int x = e[k];
+        if ((unsigned)x >= (unsigned)a.E) {
+            a.dest[p] = -1;
+            continue;
+        }
+        int pos = base[x] + __popcll(masks[wave][x] & lower);
+        for (int w = 0; w < wave; ++w) pos += __popcll(masks[w][x]);
+        a.perm[pos] = (int)p;
+        a.dest[p] = pos;
+    }
+}
+
+__global__ __launch_bounds__(256) void dispatch_gather_kernel(DispatchArgs a)
+{
+    const int t = blockIdx.x;
+    const long npos = (long)a.T * a.top_k;
+    int dst[MAX_TOPK];
+#pragma unroll
+    for (int k = 0; k < MAX_TOPK; ++k) {
+        const int v = k < a.top_k ? a.dest[(size_t)t * a.top_k + k] : -1;
+        dst[k] = (v >= 0 && v < npos) ? v : -1;
+    }
+    const int nvec = a.d / 8;
+    const u32x4 *src = (const u32x4 *)(a.x + (size_t)t * a.d);
+    for (int i = threadIdx.x; i < nvec; i += blockDim.x) {
+        const u32x4 val = src[i];
+#pragma unroll
+        for (int k = 0; k < MAX_TOPK; ++k)
+            if (dst[k] >= 0)
+                __builtin_nontemporal_store(val, (u32x4 *)(a.permuted_x + (size_t)dst[k] * a.d) + i);
+    }
+}
+
+}  // namespace
+
+static size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+size_t dispatch_workspace_bytes(int T, int E, int top_k, bool need_dest)
+{
+    const size_t nb = ((size_t)T + BT - 1) / BT;
+    size_t bytes = 2 * align256(nb * (size_t)E * sizeof(int32_t));
+    if (need_dest) bytes += align256((size_t)T * top_k * sizeof(int32_t));
+    return bytes;
+}
+
+hipError_t launch_dispatch(const DispatchArgs &a, hipStream_t stream)
+{
+    if (a.n_blocks > 0)
+        hipLaunchKernelGGL(dispatch_count_kernel, dim3(a.n_blocks), dim3(BT), 0, stream, a);
+    hipLaunchKernelGGL(dispatch_scan_kernel, dim3(1), dim3(SCAN_THREADS), 0, stream, a);
+    if (a.n_blocks > 0) {
+        hipLaunchKernelGGL(dispatch_scatter_kernel, dim3(a.n_blocks), dim3(BT), 0, stream, a);
+        hipLaunchKernelGGL(dispatch_gather_kernel, dim3(a.T), dim3(256), 0, stream, a);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace siggate

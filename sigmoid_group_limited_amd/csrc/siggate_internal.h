@@ -1,0 +1,69 @@
+// Internal declarations shared by the HIP translation units of libsiggate.
+// Not part of the public ABI (that is include/siggate.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace siggate {
+
+// k-elements of x and W staged in LDS per main-loop step
+constexpr int KC = 32;
+// tokens per dispatch block (4 waves of 64 lanes, one token per lane)
+constexpr int DISPATCH_BLOCK_TOKENS = 256;
+// largest expert count any kernel instantiates
+constexpr int MAX_EXPERTS = 384;
+// largest top_k
+constexpr int MAX_TOPK = 8;
+
+enum GateMode { MODE_SELECT = 0, MODE_LOGITS = 1, MODE_PARTIAL = 2 };
+
+struct GateArgs {
+    const uint16_t *x;      // bfloat16 bits [T, d]
+    const float *W;         // [E, d]
+    const float *bias;      // [E]
+    int T, d;
+    int n_group, topk_group, top_k, order;
+    float route_scale;
+    int chunks_total;       // ceil(d / KC)
+    int chunks_per_split;   // KC-chunks handled by one blockIdx.y
+    int n_split;            // gridDim.y of the GEMM launch
+    float *weights;         // [T, top_k]      (MODE_SELECT)
+    int32_t *indices;       // [T, top_k]      (MODE_SELECT)
+    float *logits;          // [T, E]          (MODE_LOGITS)
+    float *partial;         // [n_split, T, E] (MODE_PARTIAL, reduce input)
+};
+
+// How the logits GEMM is cut for a given T.
+struct GatePlan {
+    int m_blocks;           // 32-token MFMA blocks per wave: 1 (32 tokens/WG) or 2 (64)
+    int n_split;            // split of the k range; 1 = fused selection epilogue
+    int chunks_per_split;
+    size_t partial_bytes;   // workspace for split partials
+};
+
+GatePlan plan_gate(int T, int d, int E);
+
+// Launchers; return hipSuccess or the launch error.
+hipError_t launch_gate(const GateArgs &a, const GatePlan &p, int E, GateMode final_mode,
+                       hipStream_t stream);
+
+struct DispatchArgs {
+    const uint16_t *x;
+    const int32_t *indices;
+    int T, d, E, top_k;
+    int n_blocks;           // ceil(T / DISPATCH_BLOCK_TOKENS)
+    int32_t *block_counts;  // [n_blocks, E]  workspace
+    int32_t *block_base;    // [n_blocks, E]  workspace
+    int32_t *tokens_per_expert;  // [E]
+    int32_t *offsets;       // [E + 1] or nullptr
+    int32_t *perm;          // [T * top_k]
+    int32_t *dest;          // [T * top_k]
+    uint16_t *permuted_x;   // [T * top_k, d]
+};
+
+size_t dispatch_workspace_bytes(int T, int E, int top_k, bool need_dest);
+hipError_t launch_dispatch(const DispatchArgs &a, hipStream_t stream);
+
+}  // namespace siggate

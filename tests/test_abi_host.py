@@ -1,0 +1,130 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads, exports
+every function include/siggate.h declares, sizes workspaces, and rejects bad
+arguments before anything is enqueued."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import sigmoid_group_limited_amd as sg
+from sigmoid_group_limited_amd import binding
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                      "include", "siggate.h")
+
+DSV3 = sg.Cfg(T=64, d=7168, E=256, n_group=8, topk_group=4, top_k=8, route_scale=2.5)
+KIMI = sg.Cfg(T=256, d=7168, E=384, n_group=1, topk_group=1, top_k=8, route_scale=2.827)
+# 16-byte aligned and never dereferenced: every call below fails a host-side
+# check before anything is enqueued
+FAKE = 0x10000
+
+
+def declared_functions():
+    with open(HEADER) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(siggate_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return sg.load_library()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) == set(binding.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), f"libsiggate.so does not export {n}"
+        assert ctypes.cast(getattr(lib, n), ctypes.c_void_p).value
+
+
+def test_status_strings(lib):
+    for code in (0, -1, -2, -3, -4):
+        assert sg.siggate_status_str(code).startswith("SIGGATE_")
+    assert "unknown" in sg.siggate_status_str(7)
+
+
+def test_workspace_bytes():
+    # fused path at large T needs only the dispatch workspace
+    big = DSV3.with_T(16384)
+    nb = 16384 // 256
+    dispatch = 2 * nb * 256 * 4 + 16384 * 8 * 4
+    assert sg.siggate_workspace_bytes(big) == dispatch
+    # split-k at small T needs partial logits
+    assert sg.siggate_workspace_bytes(KIMI) >= 256 * 384 * 4 * 2
+    assert sg.siggate_workspace_bytes(sg.Cfg(0, 7168, 256, 8, 4, 8, 2.5)) == 0
+
+
+def call_forward(cfg, x=FAKE, W=FAKE, bias=FAKE, w=FAKE, i=FAKE, ws=FAKE, ws_bytes=1 << 40):
+    c = cfg.c()
+    return sg.load_library().siggate_forward(x, W, bias, ctypes.byref(c), w, i, ws, ws_bytes, None)
+
+
+def call_dispatch(cfg, x=FAKE, idx=FAKE, tpe=FAKE, off=FAKE, perm=FAKE, dest=FAKE, px=FAKE,
+                  ws=FAKE, ws_bytes=1 << 40):
+    c = cfg.c()
+    return sg.load_library().siggate_dispatch(x, idx, ctypes.byref(c), tpe, off, perm, dest, px,
+                                              ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("bad", [
+    dict(n_group=3), dict(topk_group=0), dict(topk_group=9), dict(top_k=0),
+    dict(top_k=33, topk_group=1), dict(order=2), dict(T=-1), dict(d=0),
+    dict(route_scale=float("nan")), dict(E=256, n_group=256, topk_group=1, top_k=1),
+])
+def test_forward_rejects_invalid(bad):
+    fields = DSV3.__dict__ | bad
+    assert call_forward(sg.Cfg(**fields)) == binding.SIGGATE_EINVAL
+
+
+@pytest.mark.parametrize("unsup", [
+    dict(E=64, n_group=8), dict(E=512, n_group=8), dict(E=192, n_group=8),
+    dict(n_group=128, topk_group=4, top_k=4), dict(top_k=9, topk_group=8, n_group=8),
+    dict(d=7164),
+])
+def test_forward_rejects_unsupported(unsup):
+    fields = DSV3.__dict__ | unsup
+    assert call_forward(sg.Cfg(**fields)) == binding.SIGGATE_EUNSUPPORTED
+
+
+def test_forward_pointer_and_workspace_checks():
+    assert call_forward(DSV3, x=0) == binding.SIGGATE_EINVAL
+    assert call_forward(DSV3, bias=0) == binding.SIGGATE_EINVAL
+    assert call_forward(DSV3, W=FAKE + 4) == binding.SIGGATE_EINVAL
+    assert call_forward(DSV3, w=FAKE + 8) == binding.SIGGATE_EINVAL
+    need = sg.siggate_workspace_bytes(DSV3)
+    assert need > 0
+    assert call_forward(DSV3, ws_bytes=need - 256) == binding.SIGGATE_EWORKSPACE
+    assert call_forward(DSV3, ws=0) == binding.SIGGATE_EWORKSPACE
+    # T = 0 enqueues nothing and needs no data pointers
+    assert call_forward(DSV3.with_T(0), x=0, w=0, i=0, ws=0, ws_bytes=0) == binding.SIGGATE_OK
+
+
+def test_dispatch_checks():
+    cfg = DSV3.with_T(1000)
+    assert call_dispatch(cfg.__class__(**(cfg.__dict__ | dict(E=385)))) == \
+        binding.SIGGATE_EUNSUPPORTED
+    assert call_dispatch(cfg.__class__(**(cfg.__dict__ | dict(top_k=9, E=300)))) == \
+        binding.SIGGATE_EUNSUPPORTED
+    assert call_dispatch(cfg.__class__(**(cfg.__dict__ | dict(top_k=0)))) == binding.SIGGATE_EINVAL
+    assert call_dispatch(cfg, tpe=0) == binding.SIGGATE_EINVAL
+    assert call_dispatch(cfg, perm=FAKE + 4) == binding.SIGGATE_EINVAL
+    need_with_dest = sg.siggate_workspace_bytes(cfg)
+    nb = (1000 + 255) // 256
+    cnt = ((nb * 256 * 4 + 255) // 256) * 256
+    # without a caller-provided dest the workspace must also hold it
+    assert call_dispatch(cfg, dest=0, ws_bytes=2 * cnt) == binding.SIGGATE_EWORKSPACE
+    assert need_with_dest >= 2 * cnt + 1000 * 8 * 4
+
+
+def test_python_binding_rejects_host_tensors():
+    torch = pytest.importorskip("torch")
+    x = torch.zeros((64, 7168), dtype=torch.bfloat16)
+    W = torch.zeros((256, 7168))
+    b = torch.zeros(256)
+    with pytest.raises(ValueError):
+        sg.siggate_forward(x, W, b, DSV3, weights=torch.zeros((64, 8)),
+                           indices=torch.zeros((64, 8), dtype=torch.int32),
+                           ws=torch.zeros(1 << 20, dtype=torch.uint8))

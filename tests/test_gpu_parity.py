@@ -1,0 +1,261 @@
+"""Parity of the HIP library with the CPU oracle on the same seeded inputs,
+called through the C ABI (ctypes binding).  Needs an MI355X.
+
+Small cases are compared in full; the five full-size workloads are compared
+on sampled tokens (the oracle computes them one by one) plus properties that
+hold for every token, and the dispatch is compared in full on the GPU's own
+indices."""
+import numpy as np
+import pytest
+
+import oracle
+import sigmoid_group_limited_amd as sg
+from sigmoid_group_limited_amd import workloads as wl
+from parity import (LOGIT_RTOL, check_rows_valid, compare_dispatch, compare_gate,
+                    dev_inputs, say)
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def o():
+    return oracle.load()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    sg.load_library()
+    yield
+    torch.cuda.synchronize()
+
+
+def cfg_of(gc: wl.GateConfig, T: int, d: int, order: int = 0) -> sg.Cfg:
+    return sg.Cfg(T, d, gc.n_experts, gc.n_group, gc.topk_group, gc.top_k, gc.route_scale, order)
+
+
+def run_gate(gi, cfg):
+    x, W, b = dev_inputs(gi)
+    w, i = sg.siggate_forward(x, W, b, cfg)
+    torch.cuda.synchronize()
+    return w.cpu().numpy(), i.cpu().numpy()
+
+
+def oracle_gate(o, gi, cfg, rows=None):
+    x = gi.x if rows is None else gi.x[rows]
+    return o.gate(x, gi.W, gi.bias, cfg.n_group, cfg.topk_group, cfg.top_k,
+                  cfg.route_scale, cfg.order)
+
+
+SMALL = [
+    # (name, GateConfig, T, d)
+    ("dsv3_T64", wl.DSV3, 64, 7168),
+    ("kimi_T256", wl.KIMI_K2, 256, 7168),
+    ("e128_g4_T333_d1000", wl.GateConfig(128, 4, 2, 6, 1.0), 333, 1000),
+    ("e256_g64_T97_d512", wl.GateConfig(256, 64, 16, 8, 2.5), 97, 512),
+    ("e384_g8_T1", wl.GateConfig(384, 8, 3, 8, 2.827), 1, 7168),
+    ("e256_g1_k1_T50", wl.GateConfig(256, 1, 1, 1, 1.0), 50, 7168),
+    ("e384_g2_T129_d264", wl.GateConfig(384, 2, 1, 8, 2.827), 129, 264),
+    ("e256_g8_k3_T4100_d256", wl.GateConfig(256, 8, 4, 3, 2.5), 4100, 256),
+    # fused (single k-slice) paths: 32-token and 64-token workgroups, ragged tails
+    ("dsv3_fused32_T8229_d256", wl.DSV3, 8229, 256),
+    ("kimi_fused64_T16389_d256", wl.KIMI_K2, 16389, 256),
+    ("dsv3_fused64_T16447_d200", wl.DSV3, 16447, 200),
+]
+
+
+@pytest.mark.parametrize("name,gc,T,d", SMALL, ids=[s[0] for s in SMALL])
+@pytest.mark.parametrize("order", [0, 1])
+def test_gate_parity_small(o, name, gc, T, d, order):
+    say(f"[gate] {name} order={order}")
+    gi = wl.make_gate_inputs(T, d, gc, seed=T + d)
+    cfg = cfg_of(gc, T, d, order)
+    w, i = run_gate(gi, cfg)
+    ref = oracle_gate(o, gi, cfg)
+    if order == 0:
+        stats = compare_gate(w, i, ref, gc.route_scale)
+    else:
+        # same sets and weights after sorting by expert id; order is by score
+        si = np.argsort(i, axis=1, kind="stable")
+        sr = np.argsort(ref.indices, axis=1, kind="stable")
+        ref_sorted = oracle.GateResult(np.take_along_axis(ref.weights, sr, 1),
+                                       np.take_along_axis(ref.indices, sr, 1), ref.margins)
+        stats = compare_gate(np.take_along_axis(w, si, 1), np.take_along_axis(i, si, 1),
+                             ref_sorted, gc.route_scale)
+        # order itself: where every gap between consecutive winners is
+        # clear, the sequence must equal the oracle's
+        same = np.all(np.sort(i, 1) == np.sort(ref.indices, 1), axis=1)
+        clear = same & (ref.margins[:, 0] > 1e-6)
+        x = torch.from_numpy(gi.x.view(np.int16)).cuda().view(torch.bfloat16)
+        lg = sg.siggate_logits(x, torch.from_numpy(gi.W).cuda(), cfg).cpu().numpy()
+        v = 1.0 / (1.0 + np.exp(-lg.astype(np.float64))) + gi.bias
+        vs = np.take_along_axis(v, i.astype(np.int64), 1)
+        gaps = np.min(vs[:, :-1] - vs[:, 1:], axis=1) if gc.top_k > 1 else np.full(T, 1.0)
+        strict = clear & (gaps > 1e-5)
+        assert np.array_equal(i[strict], ref.indices[strict])
+    check_rows_valid(i, gc.n_experts, gc.n_group, gc.topk_group, order)
+    say(f"    {stats}")
+
+
+@pytest.mark.parametrize("T,E,d", [(100, 256, 7168), (16384, 384, 96), (9000, 128, 40)])
+def test_logits_exact_on_integer_inputs(o, T, E, d):
+    """x small integers, W integers times 2^-8: every partial sum is exact in
+    float32, so GPU logits equal the oracle's bit for bit on both the split
+    and the fused paths."""
+    say(f"[logits-exact] T={T} E={E} d={d}")
+    rng = np.random.default_rng(T)
+    xi = rng.integers(-8, 9, size=(T, d)).astype(np.float32)
+    wi = rng.integers(-8, 9, size=(E, d))
+    x = wl.bf16_bits(xi)
+    W = (wi / 256.0).astype(np.float32)
+    cfg = sg.Cfg(T, d, E, 1, 1, 8, 1.0)
+    got = sg.siggate_logits(torch.from_numpy(x.view(np.int16)).cuda().view(torch.bfloat16),
+                            torch.from_numpy(W).cuda(), cfg).cpu().numpy()
+    rows = np.arange(T) if T <= 1000 else np.unique(np.r_[0, T - 1, rng.integers(0, T, 500)])
+    want = o.logits(x[rows], W)
+    assert np.array_equal(got[rows].astype(np.float64), want)
+
+
+@pytest.mark.parametrize("name", ["dsv3-tiny", "kimi-k2-decode", "kimi-k2-prefill"])
+def test_logits_tolerance(o, name):
+    w = wl.WORKLOADS[name]
+    say(f"[logits] {name}")
+    gi = wl.workload_inputs(w)
+    cfg = cfg_of(w.cfg, w.T, w.d)
+    x, W, _ = dev_inputs(gi)
+    got = sg.siggate_logits(x, W, cfg).cpu().numpy()
+    rng = np.random.default_rng(5)
+    rows = np.arange(w.T) if w.T <= 256 else np.unique(rng.integers(0, w.T, 256))
+    want = o.logits(gi.x[rows], gi.W)
+    err = np.abs(got[rows] - want) / np.maximum(np.abs(want), 1.0)
+    say(f"    max rel err {err.max():.3e}  max abs err {np.abs(got[rows] - want).max():.3e}")
+    assert err.max() <= LOGIT_RTOL
+
+
+@pytest.mark.parametrize("name", list(wl.WORKLOADS))
+def test_workload_full_size(o, name):
+    """Full-size workload: gate on every token, oracle on sampled tokens,
+    row properties everywhere, dispatch in full on the GPU's indices."""
+    w = wl.WORKLOADS[name]
+    say(f"[workload] {name}: T={w.T} E={w.cfg.n_experts}")
+    gi = wl.workload_inputs(w)
+    cfg = cfg_of(w.cfg, w.T, w.d)
+    x, W, b = dev_inputs(gi)
+    wg, ig = sg.siggate_forward(x, W, b, cfg)
+    torch.cuda.synchronize()
+    w_np, i_np = wg.cpu().numpy(), ig.cpu().numpy()
+    check_rows_valid(i_np, w.cfg.n_experts, w.cfg.n_group, w.cfg.topk_group)
+    rng = np.random.default_rng(7)
+    rows = np.arange(w.T) if w.T <= 256 else \
+        np.unique(np.r_[0, 1, w.T - 1, rng.integers(0, w.T, 768)])
+    ref = oracle_gate(o, gi, cfg, rows)
+    stats = compare_gate(w_np, i_np, ref, w.cfg.route_scale, rows)
+    if gi.twins:
+        dec = np.zeros(len(rows), bool)
+        for a, bb in gi.twins:
+            dec |= (ref.indices == a).any(1) ^ (ref.indices == bb).any(1)
+        stats["twin_decisive"] = int(dec.sum())
+        stats["twin_decisive_matched"] = int(np.all(i_np[rows][dec] == ref.indices[dec], 1).sum())
+        assert stats["twin_decisive_matched"] == stats["twin_decisive"], \
+            "exact twin ties must resolve to the lower expert id as in the oracle"
+    if len(gi.hot):
+        stats["hot_share"] = float(np.isin(i_np, gi.hot).mean())
+    say(f"    gate {stats}")
+    if not w.dispatch:
+        return
+    out = sg.siggate_dispatch(x, ig, cfg)
+    torch.cuda.synchronize()
+    dref = o.dispatch(i_np, w.cfg.n_experts)
+    sample = np.unique(np.r_[0, len(dref.perm) - 1, rng.integers(0, len(dref.perm), 2048)])
+    compare_dispatch(out, dref, i_np, gi.x, w.cfg.top_k, sample, o)
+    say(f"    dispatch ok: pairs={len(dref.perm)} max per expert={int(dref.counts.max())}")
+
+
+def test_zero_input_closed_form(o):
+    """x = 0: every weight is exactly route_scale / K (s = 1/2 for every
+    expert), and the selection is the group-limited top-K of the bias."""
+    gc = wl.DSV3
+    gi = wl.make_gate_inputs(300, 7168, gc, seed=3)
+    gi.x[:] = 0
+    cfg = cfg_of(gc, 300, 7168)
+    w, i = run_gate(gi, cfg)
+    assert np.all(w == np.float32(gc.route_scale / gc.top_k))
+    ref = oracle_gate(o, gi, cfg)
+    assert np.array_equal(i, ref.indices)
+
+
+def test_twin_columns_tie_exactly(o):
+    """Experts with identical W rows and bias get bit-identical logits, and
+    the lower id wins the tie when only one of them can be selected."""
+    gc = wl.KIMI_K2
+    T, d = 512, 7168
+    gi = wl.make_gate_inputs(T, d, gc, seed=9)
+    for a, b in [(3, 200), (17, 18), (100, 383)]:
+        gi.W[b] = gi.W[a]
+        gi.bias[b] = gi.bias[a]
+    cfg = cfg_of(gc, T, d)
+    x, W, _ = dev_inputs(gi)
+    lg = sg.siggate_logits(x, W, cfg).cpu().numpy()
+    for a, b in [(3, 200), (17, 18), (100, 383)]:
+        assert np.array_equal(lg[:, a], lg[:, b])
+    w, i = run_gate(gi, cfg)
+    ref = oracle_gate(o, gi, cfg)
+    compare_gate(w, i, ref, gc.route_scale)
+    for a, b in [(3, 200), (17, 18), (100, 383)]:
+        only_b = (i == b).any(1) & ~(i == a).any(1)
+        assert not only_b.any(), "the higher twin was chosen over the lower"
+
+
+def test_deterministic_repeat():
+    gc = wl.KIMI_K2
+    gi = wl.make_gate_inputs(4096, 7168, gc, seed=1)
+    x, W, b = dev_inputs(gi)
+    for T in (4096, 200):
+        cfg = cfg_of(gc, T, 7168)
+        xs = x[:T].contiguous()
+        r1 = [t.clone() for t in sg.siggate_forward(xs, W, b, cfg)]
+        r2 = sg.siggate_forward(xs, W, b, cfg)
+        assert torch.equal(r1[0], r2[0]) and torch.equal(r1[1], r2[1])
+        d1 = sg.siggate_dispatch(xs, r1[1], cfg)
+        p1 = d1.perm.clone()
+        d2 = sg.siggate_dispatch(xs, r1[1], cfg)
+        assert torch.equal(p1, d2.perm)
+
+
+@pytest.mark.parametrize("T,K,E,d,hot", [
+    (0, 8, 256, 64, False), (1, 8, 256, 64, False), (255, 8, 256, 128, False),
+    (257, 8, 384, 64, False), (1000, 3, 7, 24, False), (513, 1, 16, 8, False),
+    (70000, 8, 256, 16, True), (4097, 8, 384, 7168, False),
+])
+def test_dispatch_parity(o, T, K, E, d, hot):
+    say(f"[dispatch] T={T} K={K} E={E} d={d} hot={hot}")
+    hot_ids = np.arange(0, E, max(1, E // 16))[:16] if hot else None
+    idx = wl.random_indices(T, K, E, seed=T + E, hot=hot_ids, hot_prob=0.9) if T \
+        else np.zeros((0, K), np.int32)
+    rng = np.random.default_rng(T)
+    x = rng.integers(0, 65536, size=(T, d), dtype=np.uint16)
+    cfg = sg.Cfg(T, d, E, 1, 1, K, 1.0)
+    xd = torch.from_numpy(x.view(np.int16)).cuda().view(torch.bfloat16)
+    idd = torch.from_numpy(idx).cuda()
+    out = sg.siggate_dispatch(xd, idd, cfg)
+    torch.cuda.synchronize()
+    ref = o.dispatch(idx, E)
+    sample = None if T * K <= 20000 else np.unique(rng.integers(0, T * K, 4096))
+    compare_dispatch(out, ref, idx, x, K, sample, o)
+    # without the optional outputs the kernels use the workspace for dest
+    out2 = sg.siggate_dispatch(xd, idd, cfg, with_offsets=False, with_dest=False)
+    assert torch.equal(out2.perm, out.perm)
+    assert torch.equal(out2.tokens_per_expert, out.tokens_per_expert)
+
+
+def test_empty_batch():
+    gc = wl.DSV3
+    cfg = cfg_of(gc, 0, 7168)
+    x = torch.empty((0, 7168), dtype=torch.bfloat16, device="cuda")
+    W = torch.zeros((256, 7168), device="cuda")
+    b = torch.zeros(256, device="cuda")
+    w, i = sg.siggate_forward(x, W, b, cfg)
+    assert w.shape == (0, 8) and i.shape == (0, 8)
