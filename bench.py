@@ -1,0 +1,258 @@
+"""Throughput of the MoE gate + dispatch on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step is the whole path on one batch that is already resident in HBM:
+siggate_forward (logits GEMM + selection) followed by siggate_dispatch
+(histogram, stable permutation, row gather).  The JSON line's ``value`` is
+routed tokens/s = T / step time.  The default workload is the Kimi-K2
+prefill batch (T=16384, E=384 in one group, d=7168); the DeepSeek-V3
+prefill batch (T=16384, E=256, 8 groups keep 4) is reported beside it under
+``secondary``.
+
+``roofline`` is for the dominant kernel, the fused gate GEMM: algorithmic
+flops 2*T*d*E per launch over its average duration, measured with HIP events
+on the launch stream over the timed steps, against the fp32 MFMA peak.
+``traffic`` is read from profiles/gate_traffic.json (rocprofv3 FETCH_SIZE and
+WRITE_SIZE, scaled by a plain-copy calibration) when that file was taken
+from the current gate kernel source, else null.
+
+``cpu_baseline`` times the CPU oracle (float64, all host threads) on a
+bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_FP32_MFMA_TFLOPS = 157.3   # MI355X dense fp32 matrix peak
+PEAK_HBM_GBS = 8000.0           # MI355X HBM3E peak
+GATE_SOURCE = os.path.join(ROOT, "sigmoid_group_limited_amd", "csrc", "gate.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gate_traffic.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_sha(path: str) -> str:
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def gate_traffic(workload: str, n_launch_bytes: float):
+    """HBM bytes per gate launch from a committed counter profile of the
+    current kernel source, or None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    entry = t.get(workload)
+    if not entry or entry.get("gate_source_sha") != source_sha(GATE_SOURCE):
+        return None
+    return entry.get("hbm_bytes_per_launch")
+
+
+class Case:
+    """Device-resident inputs, outputs and workspace of one workload."""
+
+    def __init__(self, name: str):
+        import torch
+
+        import sigmoid_group_limited_amd as sg
+        from sigmoid_group_limited_amd import workloads as wl
+        self.w = wl.WORKLOADS[name]
+        c = self.w.cfg
+        t0 = time.time()
+        self.gi = wl.workload_inputs(self.w)
+        log(f"[bench] {name}: inputs drawn in {time.time() - t0:.1f}s")
+        self.cfg = sg.Cfg(self.w.T, self.w.d, c.n_experts, c.n_group, c.topk_group,
+                          c.top_k, c.route_scale)
+        dev = "cuda"
+        self.x = torch.from_numpy(self.gi.x.view(np.int16)).to(dev).view(torch.bfloat16)
+        self.W = torch.from_numpy(self.gi.W).to(dev)
+        self.b = torch.from_numpy(self.gi.bias).to(dev)
+        T, K, E, d = self.w.T, c.top_k, c.n_experts, self.w.d
+        self.weights = torch.empty((T, K), dtype=torch.float32, device=dev)
+        self.indices = torch.empty((T, K), dtype=torch.int32, device=dev)
+        self.ws = sg.workspace(self.cfg, dev)
+        self.out = sg.DispatchOut(
+            torch.empty(E, dtype=torch.int32, device=dev),
+            torch.empty(E + 1, dtype=torch.int32, device=dev),
+            torch.empty(T * K, dtype=torch.int32, device=dev),
+            torch.empty(T * K, dtype=torch.int32, device=dev),
+            torch.empty((T * K, d), dtype=torch.bfloat16, device=dev))
+        self.sg = sg
+
+    def forward(self):
+        self.sg.siggate_forward(self.x, self.W, self.b, self.cfg, self.weights,
+                                self.indices, self.ws)
+
+    def dispatch(self):
+        self.sg.siggate_dispatch(self.x, self.indices, self.cfg, self.out, self.ws)
+
+    def run(self, steps: int, warmup: int):
+        """Times ``steps`` whole steps (wall clock between two device
+        synchronisations) and, inside the same region, each stage with HIP
+        events recorded on the launch stream."""
+        import torch
+        for _ in range(warmup):
+            self.forward()
+            self.dispatch()
+        torch.cuda.synchronize()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            ev[i][0].record()
+            self.forward()
+            ev[i][1].record()
+            self.dispatch()
+            ev[i][2].record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        gate_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+        disp_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+        return wall / steps * 1e3, gate_ms, disp_ms
+
+    def algorithmic(self):
+        T, d, E, K = self.w.T, self.w.d, self.cfg.E, self.cfg.top_k
+        gate_flops = 2.0 * T * d * E
+        gate_bytes = T * d * 2 + E * d * 4 + E * 4 + T * K * 8
+        row = d * 2
+        disp_bytes = T * K * 4 + T * K * 4 * 2 + T * row + T * K * row
+        return gate_flops, gate_bytes, disp_bytes
+
+
+def cpu_baseline(case: Case, budget_s: float = 12.0):
+    """The oracle, as it stands, on the first n tokens of the workload: gate,
+    then dispatch and row gather of those tokens' pairs.  n grows from 256
+    until the run takes about budget_s / 4, then one timed run at the size
+    that fits the budget."""
+    import oracle
+    o = oracle.load()
+    c = case.cfg
+    gi = case.gi
+
+    def one(n):
+        t0 = time.perf_counter()
+        r = o.gate(gi.x[:n], gi.W, gi.bias, c.n_group, c.topk_group, c.top_k, c.route_scale)
+        dr = o.dispatch(r.indices, c.E)
+        o.gather_rows(gi.x[:n], dr.perm, c.top_k)
+        return time.perf_counter() - t0
+
+    n = 256
+    dt = one(n)
+    while dt < budget_s / 4 and n * 2 <= case.w.T:
+        n *= 2
+        dt = one(n)
+    if dt < budget_s / 2:
+        n_final = min(case.w.T, int(n * (budget_s / 2) / max(dt, 1e-3)))
+        n_final = max(n, n_final // 256 * 256)
+        if n_final != n:
+            n = n_final
+            dt = one(n)
+    return dict(value=n / dt, unit="tokens/s", cores=o.num_threads(), kind="oracle",
+                sample=f"first {n} of {case.w.T} tokens of {case.w.name}: float64 gate, "
+                       f"dispatch and row gather of their {n * c.top_k} pairs; {dt:.2f} s")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="kimi-k2-prefill")
+    ap.add_argument("--secondary", default="dsv3-prefill-ties")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this path runs on a single MI355X "
+              "(sharding is by tokens and needs no exchange for the gate); "
+              "run it with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        a = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n, "launches": 3}))
+        return
+
+    case = Case(args.workload)
+    ms, gate_ms, disp_ms = case.run(args.steps, args.warmup)
+    T = case.w.T
+    flops, gate_bytes, disp_bytes = case.algorithmic()
+    achieved = flops / (gate_ms * 1e-3) / 1e12
+    traffic = gate_traffic(case.w.name, gate_bytes)
+    result = {
+        "metric": "routed tokens/s (gate+dispatch)",
+        "value": T / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded; x ~ N(0,1) in bfloat16, W ~ N(0,1/d), bias ~ U(-0.05,0.05))",
+        "config": {"workload": case.w.name, "T": T, "d": case.w.d, "E": case.cfg.E,
+                   "n_group": case.cfg.n_group, "topk_group": case.cfg.topk_group,
+                   "top_k": case.cfg.top_k, "route_scale": case.cfg.route_scale,
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_FP32_MFMA_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_FP32_MFMA_TFLOPS,
+                     "traffic": traffic},
+        "stages": {
+            "gate_ms": gate_ms, "dispatch_ms": disp_ms,
+            "gate_tflops": achieved,
+            "dispatch_algorithmic_GBps": disp_bytes / (disp_ms * 1e-3) / 1e9,
+            "dispatch_hbm_frac": disp_bytes / (disp_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+            "roofline_tokens_per_s": T / (flops / (PEAK_FP32_MFMA_TFLOPS * 1e12)
+                                          + disp_bytes / (PEAK_HBM_GBS * 1e9)),
+        },
+    }
+    result["stages"]["path_roofline_frac"] = result["value"] / result["stages"]["roofline_tokens_per_s"]
+    if args.secondary:
+        sec = Case(args.secondary)
+        ms2, g2, d2 = sec.run(args.steps, args.warmup)
+        f2, _, db2 = sec.algorithmic()
+        result["secondary"] = {
+            "workload": sec.w.name, "E": sec.cfg.E, "value": sec.w.T / (ms2 * 1e-3),
+            "ms_per_step": ms2, "gate_ms": g2, "dispatch_ms": d2,
+            "gate_tflops": f2 / (g2 * 1e-3) / 1e12,
+            "gate_mfma_frac": f2 / (g2 * 1e-3) / 1e12 / PEAK_FP32_MFMA_TFLOPS,
+            "dispatch_algorithmic_GBps": db2 / (d2 * 1e-3) / 1e9,
+        }
+        del sec
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(case)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
