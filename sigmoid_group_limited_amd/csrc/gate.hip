@@ -32,12 +32,16 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int NT = 256;         // threads per workgroup (4 waves)
+constexpr int RED_NT = 256;     // threads per workgroup of the split-k reduction
 constexpr int KPAD = KC + 4;    // padded LDS row in floats: rows start 4 banks apart
 
-template <int E, int MB>
+// Workgroup of NW waves: 4 expert quarters x NW/4 token splits.
+template <int E, int MB, int NW>
 struct Shape {
+    static constexpr int NT = 64 * NW;          // threads per workgroup
     static constexpr int BM = 32 * MB;          // tokens per workgroup
+    static constexpr int WM = NW / 4;           // token splits
+    static constexpr int MBW = MB / WM;         // 32-token MFMA blocks per wave
     static constexpr int NB = E / 128;          // 32-expert MFMA blocks per wave
     static constexpr int WCOLS = E / 4;         // experts per wave
     static constexpr int V = E / 64;            // experts per lane in the selection
@@ -46,6 +50,8 @@ struct Shape {
     static constexpr int EPI = BM * LROW;
     static constexpr int SMEM = STAGE > EPI ? STAGE : EPI;
     static_assert(E % 128 == 0, "E must be a multiple of 128");
+    static_assert(NW % 4 == 0 && MB % WM == 0, "waves must tile the workgroup");
+    static_assert(KC * BM / NT >= 4, "each thread stages at least 4 bfloat16 of x");
 };
 
 __device__ __forceinline__ float bf16_lo(unsigned w) { return __uint_as_float(w << 16); }
@@ -59,23 +65,24 @@ __device__ __forceinline__ uint32_t orderable(float f)
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m)
-{
-    const int lo = __shfl_xor((int)(uint32_t)v, m);
-    const int hi = __shfl_xor((int)(uint32_t)(v >> 32), m);
-    return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
-}
-
 __device__ __forceinline__ float readlane_f(float v, int lane)
 {
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
 }
 
-// Selection for one token held by one wave: lane l owns experts
-// [l*V, l*V + V) and their logits lg[].  Writes weights/indices row t.
+// Selection for one token held by one wave.  Lane l owns experts
+// [l*V, l*V + V) and their logits lg[].  `scratch` is wave-private LDS of at
+// least 3 * MAX_TOPK words.  Writes row t of weights and indices.
+//
+// The K winners are the K largest choice scores under (v desc, id asc).
+// Scores map to order-preserving uint32 keys; the K-th largest key is found
+// bit by bit from the top (a count of keys >= candidate is one ballot per
+// owned expert), then every key above it is selected and keys equal to it
+// are taken in ascending expert id until K are chosen.
 template <int V>
 __device__ __forceinline__ void select_token(const float (&lg)[V], const float (&bias_r)[V],
-                                             const int lane, const GateArgs &a, const int t)
+                                             const int lane, const GateArgs &a, const int t,
+                                             float *scratch)
 {
     float s[V], v[V];
 #pragma unroll
@@ -122,80 +129,83 @@ __device__ __forceinline__ void select_token(const float (&lg)[V], const float (
         }
     }
 
-    // Token top-K: K rounds of a wave-wide arg-max under (v desc, id asc).
     const int K = a.top_k;
-    int sel_i[MAX_TOPK];
-    float sel_s[MAX_TOPK];
+    uint32_t key[V];
 #pragma unroll
-    for (int k = 0; k < MAX_TOPK; ++k) {
-        sel_i[k] = 0x7fffffff;
-        sel_s[k] = 0.0f;
-        if (k < K) {
-            float bv = v[0];
-            int bj = 0;
+    for (int j = 0; j < V; ++j) key[j] = orderable(v[j] + 0.0f);   // -0 -> +0
+
+    // K-th largest key, most significant bit first.
+    uint32_t kth = 0;
+    for (int b = 31; b >= 0; --b) {
+        const uint32_t cand = kth | (1u << b);
+        int cnt = 0;
 #pragma unroll
-            for (int j = 1; j < V; ++j) {
-                if (v[j] > bv) {
-                    bv = v[j];
-                    bj = j;
-                }
-            }
-            uint64_t key = ((uint64_t)orderable(bv) << 32) |
-                           (uint32_t)(0xffffffffu - (uint32_t)(lane * V + bj));
-#pragma unroll
-            for (int off = 32; off >= 1; off >>= 1) {
-                const uint64_t o = shfl_xor_u64(key, off);
-                key = o > key ? o : key;
-            }
-            const int win = __builtin_amdgcn_readfirstlane((int)(0xffffffffu - (uint32_t)key));
-            const int owner = win / V;
-            const int wj = win - owner * V;
-            float mine = 0.0f;
-#pragma unroll
-            for (int j = 0; j < V; ++j)
-                if (j == wj) mine = s[j];
-            sel_s[k] = readlane_f(mine, owner);
-            sel_i[k] = win;
-            if (lane == owner) {
-#pragma unroll
-                for (int j = 0; j < V; ++j)
-                    if (j == wj) v[j] = -INFINITY;
-            }
-        }
+        for (int j = 0; j < V; ++j) cnt += __popcll(__ballot(key[j] >= cand));
+        if (cnt >= K) kth = cand;
     }
 
-    // Renormalise over the K winners (unbiased s) and scale.
+    // Keys above kth are in; keys equal to kth fill the rest by ascending id
+    // (id = lane*V + j, so lower lanes first, then lower j).
+    const uint64_t below = (1ull << lane) - 1ull;
+    int above = 0, eq_before = 0;
+#pragma unroll
+    for (int j = 0; j < V; ++j) {
+        above += __popcll(__ballot(key[j] > kth));
+        eq_before += __popcll(__ballot(key[j] == kth) & below);
+    }
+    const int need = K - above;
+    bool sel[V];
+    int sel_before = 0;
+#pragma unroll
+    for (int j = 0; j < V; ++j) {
+        const bool eq = key[j] == kth;
+        sel[j] = key[j] > kth || (eq && eq_before < need);
+        eq_before += eq;
+    }
+#pragma unroll
+    for (int j = 0; j < V; ++j) sel_before += __popcll(__ballot(sel[j]) & below);
+
+    // Compact the winners in ascending id into scratch: [0,K) scores s,
+    // [K,2K) ids, [2K,3K) keys.
+    int p = sel_before;
+#pragma unroll
+    for (int j = 0; j < V; ++j) {
+        if (sel[j]) {
+            scratch[p] = s[j];
+            scratch[MAX_TOPK + p] = __int_as_float(lane * V + j);
+            scratch[2 * MAX_TOPK + p] = __uint_as_float(key[j]);
+            ++p;
+        }
+    }
+    __builtin_amdgcn_wave_barrier();
+
+    // Renormalise over the K winners (unbiased s, summed in ascending id
+    // order) and scale; lane k < K writes one entry.
     float denom = 0.0f;
-#pragma unroll
-    for (int k = 0; k < MAX_TOPK; ++k)
-        if (k < K) denom += sel_s[k];
-
-    int my_i = 0;
-    float my_s = 0.0f;
-#pragma unroll
-    for (int k = 0; k < MAX_TOPK; ++k) {
-        if (k < K && lane == k) {
-            my_i = sel_i[k];
-            my_s = sel_s[k];
-        }
-    }
-    int pos = lane;
-    if (a.order == 0) {   // ascending expert id
-        pos = 0;
-#pragma unroll
-        for (int k = 0; k < MAX_TOPK; ++k)
-            if (k < K) pos += sel_i[k] < my_i;
-    }
+    for (int k = 0; k < K; ++k) denom += scratch[k];
     if (lane < K) {
+        const float my_s = scratch[lane];
+        const int my_i = __float_as_int(scratch[MAX_TOPK + lane]);
+        int pos = lane;
+        if (a.order == 1) {   // choice score descending, id ascending on ties
+            const uint32_t my_key = __float_as_uint(scratch[2 * MAX_TOPK + lane]);
+            pos = 0;
+            for (int k = 0; k < K; ++k) {
+                const uint32_t kk = __float_as_uint(scratch[2 * MAX_TOPK + k]);
+                pos += kk > my_key || (kk == my_key && k < lane);
+            }
+        }
         a.indices[(size_t)t * K + pos] = my_i;
         a.weights[(size_t)t * K + pos] = my_s / denom * a.route_scale;
     }
+    __builtin_amdgcn_wave_barrier();
 }
 
-template <int E, int MB, int MODE>
-__global__ __launch_bounds__(NT) void gate_gemm_kernel(GateArgs a)
+template <int E, int MB, int NW, int MODE>
+__global__ __launch_bounds__(64 * NW) void gate_gemm_kernel(GateArgs a)
 {
-    using S = Shape<E, MB>;
+    using S = Shape<E, MB, NW>;
+    constexpr int NT = S::NT;
     __shared__ __attribute__((aligned(16))) float smem[S::SMEM];
     float *const Ws = smem;                    // [2][E][KPAD]
     float *const Xs = smem + 2 * E * KPAD;     // [2][BM][KPAD]
@@ -203,54 +213,68 @@ __global__ __launch_bounds__(NT) void gate_gemm_kernel(GateArgs a)
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
+    const int wn = wave & 3;            // expert quarter of this wave
+    const int wm = wave >> 2;           // token split of this wave
     const int t0 = blockIdx.x * S::BM;
     const int d = a.d;
     const int c_begin = blockIdx.y * a.chunks_per_split;
     const int c_end = min(c_begin + a.chunks_per_split, a.chunks_total);
 
-    // ---- global -> register staging: W rows (tid/8) + 32 i, 4 floats at
-    // column (tid%8)*4; x row tid/4, 8 bfloat16 at column (tid%4)*8.
-    constexpr int WLOADS = E / 32;
-    f32x4 wreg[WLOADS];
-    u32x4 xreg;
+    // ---- global -> register staging.  Thread tid loads W rows
+    // (tid/8) + (NT/8) i, 4 floats at column (tid%8)*4, and x row tid/XT, KC/XT
+    // bfloat16 at column (tid%XT)*(KC/XT).  The steady-state loop has no
+    // branches: columns past d (last chunk only) read a clamped in-range
+    // address and are zeroed when written to LDS; rows past T read row T-1
+    // and their logits are dropped.
+    constexpr int WLOADS = E * 8 / NT;
+    constexpr int XT = NT / S::BM;          // threads per x row: 4 or 8
+    constexpr int XE = KC / XT;             // bfloat16 per thread: 8 or 4
+    typedef unsigned int xvec __attribute__((ext_vector_type(XE / 2)));
+    struct Stage {
+        f32x4 w[WLOADS];
+        xvec x;
+    };
     const int w_row = tid >> 3;
     const int w_col = (tid & 7) * 4;
-    const int x_row = tid >> 2;
-    const int x_col = (tid & 3) * 8;
-    const bool x_thread = x_row < S::BM;
-    const bool x_valid = x_thread && (t0 + x_row) < a.T;
-    const float *const Wp = a.W + (size_t)w_row * d + w_col;
-    const uint16_t *const Xp = a.x + (size_t)(x_valid ? t0 + x_row : 0) * d + x_col;
+    const int x_row = tid / XT;
+    const int x_col = (tid % XT) * XE;
+    const int x_t = min(t0 + x_row, a.T - 1);
+    const float *const Wp = a.W + (size_t)w_row * d;
+    const uint16_t *const Xp = a.x + (size_t)x_t * d;
 
-    auto load_global = [&](int c) {
+    auto load_global = [&](int c, Stage &st) {
+        const int k0 = c * KC;
+        const int wc = min(k0 + w_col, d - 4);
+        const int xc = min(k0 + x_col, d - XE);
+#pragma unroll
+        for (int i = 0; i < WLOADS; ++i)
+            st.w[i] = *(const f32x4 *)(Wp + (size_t)i * (NT / 8) * d + wc);
+        st.x = *(const xvec *)(Xp + xc);
+    };
+    auto store_lds = [&](int c, int buf, const Stage &st) {
         const int k0 = c * KC;
         const bool wk = k0 + w_col < d;
-#pragma unroll
-        for (int i = 0; i < WLOADS; ++i)
-            wreg[i] = wk ? *(const f32x4 *)(Wp + (size_t)i * 32 * d + k0) : f32x4{0.f, 0.f, 0.f, 0.f};
-        const bool xk = x_valid && k0 + x_col < d;
-        xreg = xk ? *(const u32x4 *)(Xp + k0) : u32x4{0u, 0u, 0u, 0u};
-    };
-    auto store_lds = [&](int buf) {
+        const bool xk = k0 + x_col < d;
         float *wb = Ws + buf * E * KPAD;
+        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int i = 0; i < WLOADS; ++i)
-            *(f32x4 *)(wb + (w_row + 32 * i) * KPAD + w_col) = wreg[i];
-        if (x_thread) {
-            float *xb = Xs + buf * S::BM * KPAD + x_row * KPAD + x_col;
-            const f32x4 lo = {bf16_lo(xreg[0]), bf16_hi(xreg[0]), bf16_lo(xreg[1]), bf16_hi(xreg[1])};
-            const f32x4 hi = {bf16_lo(xreg[2]), bf16_hi(xreg[2]), bf16_lo(xreg[3]), bf16_hi(xreg[3])};
-            *(f32x4 *)xb = lo;
-            *(f32x4 *)(xb + 4) = hi;
+            *(f32x4 *)(wb + (w_row + (NT / 8) * i) * KPAD + w_col) = wk ? st.w[i] : zero;
+        float *xb = Xs + buf * S::BM * KPAD + x_row * KPAD + x_col;
+#pragma unroll
+        for (int h = 0; h < XE / 4; ++h) {
+            const unsigned u0 = xk ? st.x[2 * h] : 0u;
+            const unsigned u1 = xk ? st.x[2 * h + 1] : 0u;
+            *(f32x4 *)(xb + 4 * h) = f32x4{bf16_lo(u0), bf16_hi(u0), bf16_lo(u1), bf16_hi(u1)};
         }
     };
 
     // ---- MFMA main loop.  For a group of 8 k-columns, lane l reads 4
     // consecutive k of row (l%32) at offset 4*(l/32); MFMA j pairs column j
     // (lanes 0-31) with column 4+j (lanes 32-63) for A and B alike.
-    f32x16 acc[MB][S::NB];
+    f32x16 acc[S::MBW][S::NB];
 #pragma unroll
-    for (int m = 0; m < MB; ++m)
+    for (int m = 0; m < S::MBW; ++m)
 #pragma unroll
         for (int n = 0; n < S::NB; ++n)
 #pragma unroll
@@ -258,14 +282,15 @@ __global__ __launch_bounds__(NT) void gate_gemm_kernel(GateArgs a)
 
     const int f_row = lane & 31;
     const int f_k = (lane >> 5) * 4;
-    auto compute = [&](int buf) {
-        const float *xb = Xs + buf * S::BM * KPAD;
-        const float *wb = Ws + buf * E * KPAD + wave * S::WCOLS * KPAD;
+    // MFMAs of the 8-column groups [c8_begin, c8_end) of LDS buffer buf
+    auto compute = [&](int buf, int c8_begin, int c8_end) {
+        const float *xb = Xs + buf * S::BM * KPAD + wm * S::MBW * 32 * KPAD;
+        const float *wb = Ws + buf * E * KPAD + wn * S::WCOLS * KPAD;
 #pragma unroll
-        for (int c8 = 0; c8 < KC / 8; ++c8) {
-            f32x4 af[MB], bf[S::NB];
+        for (int c8 = c8_begin; c8 < c8_end; ++c8) {
+            f32x4 af[S::MBW], bf[S::NB];
 #pragma unroll
-            for (int m = 0; m < MB; ++m)
+            for (int m = 0; m < S::MBW; ++m)
                 af[m] = *(const f32x4 *)(xb + (m * 32 + f_row) * KPAD + c8 * 8 + f_k);
 #pragma unroll
             for (int n = 0; n < S::NB; ++n)
@@ -273,7 +298,7 @@ __global__ __launch_bounds__(NT) void gate_gemm_kernel(GateArgs a)
 #pragma unroll
             for (int j = 0; j < 4; ++j)
 #pragma unroll
-                for (int m = 0; m < MB; ++m)
+                for (int m = 0; m < S::MBW; ++m)
 #pragma unroll
                     for (int n = 0; n < S::NB; ++n)
                         acc[m][n] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[m][j], bf[n][j],
@@ -281,29 +306,48 @@ __global__ __launch_bounds__(NT) void gate_gemm_kernel(GateArgs a)
         }
     };
 
+    // Pipeline over KC-column chunks.  While chunk c feeds the matrix cores
+    // from one LDS buffer, chunks c+1 and c+2 wait in two register stages.
+    // Halfway through chunk c, chunk c+1 is written to the other LDS buffer
+    // and its register stage is refilled with chunk c+3, so every global
+    // load has two chunks of MFMA work to land in.  The one barrier per
+    // chunk sits at its end, when the LDS writes have long completed.  The
+    // stages alternate, so the loop handles chunks in pairs (static indices).
+    // Past the last chunk, loads and stores repeat the last chunk (never
+    // read) instead of branching.
     if (c_begin < c_end) {
-        load_global(c_begin);
-        store_lds(0);
-        __syncthreads();
-        for (int c = c_begin; c < c_end; ++c) {
-            const int buf = (c - c_begin) & 1;
-            const bool more = c + 1 < c_end;
-            if (more) load_global(c + 1);
-            compute(buf);
-            if (more) store_lds(buf ^ 1);
+        const int c_last = c_end - 1;
+        Stage stA, stB;
+        auto step = [&](int c, int buf, Stage &st) {
+            compute(buf, 0, KC / 16);
+            store_lds(min(c + 1, c_last), buf ^ 1, st);
+            load_global(min(c + 3, c_last), st);
+            compute(buf, KC / 16, KC / 8);
             __syncthreads();
+        };
+        load_global(c_begin, stA);
+        load_global(min(c_begin + 1, c_last), stB);
+        store_lds(c_begin, 0, stA);
+        load_global(min(c_begin + 2, c_last), stA);
+        __syncthreads();
+        int c = c_begin;
+        for (; c + 1 < c_end; c += 2) {
+            step(c, 0, stB);        // stores chunk c+1 (stB), refills stB with c+3
+            step(c + 1, 1, stA);    // stores chunk c+2 (stA), refills stA with c+4
         }
+        if (c < c_end) step(c, 0, stB);
     }
 
     // Accumulator element r of block (m, n) in lane l is token
-    // m*32 + 8*(r/4) + 4*(l/32) + r%4 and expert wave*E/4 + n*32 + l%32.
-    const int e_base = wave * S::WCOLS + (lane & 31);
-    const int r_base = 4 * (lane >> 5);
+    // (wm*MBW + m)*32 + 8*(r/4) + 4*(l/32) + r%4 and expert
+    // wn*E/4 + n*32 + l%32.
+    const int e_base = wn * S::WCOLS + (lane & 31);
+    const int r_base = wm * S::MBW * 32 + 4 * (lane >> 5);
 
     if constexpr (MODE == MODE_PARTIAL || MODE == MODE_LOGITS) {
         float *out = MODE == MODE_PARTIAL ? a.partial + (size_t)blockIdx.y * a.T * E : a.logits;
 #pragma unroll
-        for (int m = 0; m < MB; ++m)
+        for (int m = 0; m < S::MBW; ++m)
 #pragma unroll
             for (int n = 0; n < S::NB; ++n)
 #pragma unroll
@@ -312,11 +356,11 @@ __global__ __launch_bounds__(NT) void gate_gemm_kernel(GateArgs a)
                     if (t < a.T) out[(size_t)t * E + e_base + n * 32] = acc[m][n][r];
                 }
     } else {
-        // Scores go to LDS (never to HBM); each wave then selects for BM/4
+        // Scores go to LDS (never to HBM); each wave then selects for BM/NW
         // tokens.
         float *const Ls = smem;   // [BM][LROW]
 #pragma unroll
-        for (int m = 0; m < MB; ++m)
+        for (int m = 0; m < S::MBW; ++m)
 #pragma unroll
             for (int n = 0; n < S::NB; ++n)
 #pragma unroll
@@ -331,14 +375,16 @@ __global__ __launch_bounds__(NT) void gate_gemm_kernel(GateArgs a)
 #pragma unroll
         for (int j = 0; j < V; ++j) bias_r[j] = a.bias[lane * V + j];
 
-        for (int i = 0; i < S::BM / 4; ++i) {
-            const int row = wave * (S::BM / 4) + i;
+        for (int i = 0; i < S::BM / NW; ++i) {
+            const int row = wave * (S::BM / NW) + i;
             const int t = t0 + row;
             if (t >= a.T) break;
             float lg[V];
 #pragma unroll
             for (int j = 0; j < V; ++j) lg[j] = Ls[row * S::LROW + lane * V + j];
-            select_token<V>(lg, bias_r, lane, a, t);
+            // the row is dead once read: it doubles as the wave's scratch
+            __builtin_amdgcn_wave_barrier();
+            select_token<V>(lg, bias_r, lane, a, t, Ls + row * S::LROW);
         }
     }
 }
@@ -346,11 +392,12 @@ __global__ __launch_bounds__(NT) void gate_gemm_kernel(GateArgs a)
 // Adds the n_split partial logits of one token (fixed order s = 0, 1, ...)
 // and writes the logits or runs the selection.  One wave per token.
 template <int E, int MODE>
-__global__ __launch_bounds__(NT) void gate_reduce_kernel(GateArgs a)
+__global__ __launch_bounds__(RED_NT) void gate_reduce_kernel(GateArgs a)
 {
     constexpr int V = E / 64;
+    __shared__ float scratch[RED_NT / 64][3 * MAX_TOPK];
     const int lane = threadIdx.x & 63;
-    const int t = blockIdx.x * (NT / 64) + (threadIdx.x >> 6);
+    const int t = blockIdx.x * (RED_NT / 64) + (threadIdx.x >> 6);
     if (t >= a.T) return;
     float lg[V];
 #pragma unroll
@@ -367,7 +414,7 @@ __global__ __launch_bounds__(NT) void gate_reduce_kernel(GateArgs a)
         float bias_r[V];
 #pragma unroll
         for (int j = 0; j < V; ++j) bias_r[j] = a.bias[lane * V + j];
-        select_token<V>(lg, bias_r, lane, a, t);
+        select_token<V>(lg, bias_r, lane, a, t, scratch[threadIdx.x >> 6]);
     }
 }
 
@@ -375,29 +422,31 @@ template <int E>
 hipError_t launch_for_e(const GateArgs &a, const GatePlan &p, GateMode final_mode,
                         hipStream_t stream)
 {
-    const dim3 block(NT);
     if (p.n_split == 1) {
         const int bm = 32 * p.m_blocks;
         const dim3 grid((a.T + bm - 1) / bm, 1);
         if (p.m_blocks == 2) {
+            // 64 tokens: 8 waves, two per SIMD
+            const dim3 block(64 * 8);
             if (final_mode == MODE_SELECT)
-                hipLaunchKernelGGL((gate_gemm_kernel<E, 2, MODE_SELECT>), grid, block, 0, stream, a);
+                hipLaunchKernelGGL((gate_gemm_kernel<E, 2, 8, MODE_SELECT>), grid, block, 0, stream, a);
             else
-                hipLaunchKernelGGL((gate_gemm_kernel<E, 2, MODE_LOGITS>), grid, block, 0, stream, a);
+                hipLaunchKernelGGL((gate_gemm_kernel<E, 2, 8, MODE_LOGITS>), grid, block, 0, stream, a);
         } else {
+            const dim3 block(64 * 4);
             if (final_mode == MODE_SELECT)
-                hipLaunchKernelGGL((gate_gemm_kernel<E, 1, MODE_SELECT>), grid, block, 0, stream, a);
+                hipLaunchKernelGGL((gate_gemm_kernel<E, 1, 4, MODE_SELECT>), grid, block, 0, stream, a);
             else
-                hipLaunchKernelGGL((gate_gemm_kernel<E, 1, MODE_LOGITS>), grid, block, 0, stream, a);
+                hipLaunchKernelGGL((gate_gemm_kernel<E, 1, 4, MODE_LOGITS>), grid, block, 0, stream, a);
         }
     } else {
         const dim3 grid((a.T + 31) / 32, p.n_split);
-        hipLaunchKernelGGL((gate_gemm_kernel<E, 1, MODE_PARTIAL>), grid, block, 0, stream, a);
+        hipLaunchKernelGGL((gate_gemm_kernel<E, 1, 4, MODE_PARTIAL>), grid, dim3(256), 0, stream, a);
         const dim3 rgrid((a.T + 3) / 4);
         if (final_mode == MODE_SELECT)
-            hipLaunchKernelGGL((gate_reduce_kernel<E, MODE_SELECT>), rgrid, block, 0, stream, a);
+            hipLaunchKernelGGL((gate_reduce_kernel<E, MODE_SELECT>), rgrid, dim3(RED_NT), 0, stream, a);
         else
-            hipLaunchKernelGGL((gate_reduce_kernel<E, MODE_LOGITS>), rgrid, block, 0, stream, a);
+            hipLaunchKernelGGL((gate_reduce_kernel<E, MODE_LOGITS>), rgrid, dim3(RED_NT), 0, stream, a);
     }
     return hipGetLastError();
 }
