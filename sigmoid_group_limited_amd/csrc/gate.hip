@@ -201,143 +201,17 @@ __device__ __forceinline__ void select_token(const float (&lg)[V], const float (
     __builtin_amdgcn_wave_barrier();
 }
 
+// Writes a finished BM x E logits tile: as partial or final logits, or
+// through LDS (never HBM) into the selection, BM/NW tokens per wave.
 template <int E, int MB, int NW, int MODE>
-__global__ __launch_bounds__(64 * NW) void gate_gemm_kernel(GateArgs a)
+__device__ __forceinline__ void finish_tile(const GateArgs &a,
+                                            f32x16 (&acc)[Shape<E, MB, NW>::MBW][Shape<E, MB, NW>::NB],
+                                            float *smem, const int t0, const int wave,
+                                            const int lane)
 {
     using S = Shape<E, MB, NW>;
-    constexpr int NT = S::NT;
-    __shared__ __attribute__((aligned(16))) float smem[S::SMEM];
-    float *const Ws = smem;                    // [2][E][KPAD]
-    float *const Xs = smem + 2 * E * KPAD;     // [2][BM][KPAD]
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int wn = wave & 3;            // expert quarter of this wave
-    const int wm = wave >> 2;           // token split of this wave
-    const int t0 = blockIdx.x * S::BM;
-    const int d = a.d;
-    const int c_begin = blockIdx.y * a.chunks_per_split;
-    const int c_end = min(c_begin + a.chunks_per_split, a.chunks_total);
-
-    // ---- global -> register staging.  Thread tid loads W rows
-    // (tid/8) + (NT/8) i, 4 floats at column (tid%8)*4, and x row tid/XT, KC/XT
-    // bfloat16 at column (tid%XT)*(KC/XT).  The steady-state loop has no
-    // branches: columns past d (last chunk only) read a clamped in-range
-    // address and are zeroed when written to LDS; rows past T read row T-1
-    // and their logits are dropped.
-    constexpr int WLOADS = E * 8 / NT;
-    constexpr int XT = NT / S::BM;          // threads per x row: 4 or 8
-    constexpr int XE = KC / XT;             // bfloat16 per thread: 8 or 4
-    typedef unsigned int xvec __attribute__((ext_vector_type(XE / 2)));
-    struct Stage {
-        f32x4 w[WLOADS];
-        xvec x;
-    };
-    const int w_row = tid >> 3;
-    const int w_col = (tid & 7) * 4;
-    const int x_row = tid / XT;
-    const int x_col = (tid % XT) * XE;
-    const int x_t = min(t0 + x_row, a.T - 1);
-    const float *const Wp = a.W + (size_t)w_row * d;
-    const uint16_t *const Xp = a.x + (size_t)x_t * d;
-
-    auto load_global = [&](int c, Stage &st) {
-        const int k0 = c * KC;
-        const int wc = min(k0 + w_col, d - 4);
-        const int xc = min(k0 + x_col, d - XE);
-#pragma unroll
-        for (int i = 0; i < WLOADS; ++i)
-            st.w[i] = *(const f32x4 *)(Wp + (size_t)i * (NT / 8) * d + wc);
-        st.x = *(const xvec *)(Xp + xc);
-    };
-    auto store_lds = [&](int c, int buf, const Stage &st) {
-        const int k0 = c * KC;
-        const bool wk = k0 + w_col < d;
-        const bool xk = k0 + x_col < d;
-        float *wb = Ws + buf * E * KPAD;
-        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int i = 0; i < WLOADS; ++i)
-            *(f32x4 *)(wb + (w_row + (NT / 8) * i) * KPAD + w_col) = wk ? st.w[i] : zero;
-        float *xb = Xs + buf * S::BM * KPAD + x_row * KPAD + x_col;
-#pragma unroll
-        for (int h = 0; h < XE / 4; ++h) {
-            const unsigned u0 = xk ? st.x[2 * h] : 0u;
-            const unsigned u1 = xk ? st.x[2 * h + 1] : 0u;
-            *(f32x4 *)(xb + 4 * h) = f32x4{bf16_lo(u0), bf16_hi(u0), bf16_lo(u1), bf16_hi(u1)};
-        }
-    };
-
-    // ---- MFMA main loop.  For a group of 8 k-columns, lane l reads 4
-    // consecutive k of row (l%32) at offset 4*(l/32); MFMA j pairs column j
-    // (lanes 0-31) with column 4+j (lanes 32-63) for A and B alike.
-    f32x16 acc[S::MBW][S::NB];
-#pragma unroll
-    for (int m = 0; m < S::MBW; ++m)
-#pragma unroll
-        for (int n = 0; n < S::NB; ++n)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[m][n][r] = 0.0f;
-
-    const int f_row = lane & 31;
-    const int f_k = (lane >> 5) * 4;
-    // MFMAs of the 8-column groups [c8_begin, c8_end) of LDS buffer buf
-    auto compute = [&](int buf, int c8_begin, int c8_end) {
-        const float *xb = Xs + buf * S::BM * KPAD + wm * S::MBW * 32 * KPAD;
-        const float *wb = Ws + buf * E * KPAD + wn * S::WCOLS * KPAD;
-#pragma unroll
-        for (int c8 = c8_begin; c8 < c8_end; ++c8) {
-            f32x4 af[S::MBW], bf[S::NB];
-#pragma unroll
-            for (int m = 0; m < S::MBW; ++m)
-                af[m] = *(const f32x4 *)(xb + (m * 32 + f_row) * KPAD + c8 * 8 + f_k);
-#pragma unroll
-            for (int n = 0; n < S::NB; ++n)
-                bf[n] = *(const f32x4 *)(wb + (n * 32 + f_row) * KPAD + c8 * 8 + f_k);
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-#pragma unroll
-                for (int m = 0; m < S::MBW; ++m)
-#pragma unroll
-                    for (int n = 0; n < S::NB; ++n)
-                        acc[m][n] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[m][j], bf[n][j],
-                                                                         acc[m][n], 0, 0, 0);
-        }
-    };
-
-    // Pipeline over KC-column chunks.  While chunk c feeds the matrix cores
-    // from one LDS buffer, chunks c+1 and c+2 wait in two register stages.
-    // Halfway through chunk c, chunk c+1 is written to the other LDS buffer
-    // and its register stage is refilled with chunk c+3, so every global
-    // load has two chunks of MFMA work to land in.  The one barrier per
-    // chunk sits at its end, when the LDS writes have long completed.  The
-    // stages alternate, so the loop handles chunks in pairs (static indices).
-    // Past the last chunk, loads and stores repeat the last chunk (never
-    // read) instead of branching.
-    if (c_begin < c_end) {
-        const int c_last = c_end - 1;
-        Stage stA, stB;
-        auto step = [&](int c, int buf, Stage &st) {
-            compute(buf, 0, KC / 16);
-            store_lds(min(c + 1, c_last), buf ^ 1, st);
-            load_global(min(c + 3, c_last), st);
-            compute(buf, KC / 16, KC / 8);
-            __syncthreads();
-        };
-        load_global(c_begin, stA);
-        load_global(min(c_begin + 1, c_last), stB);
-        store_lds(c_begin, 0, stA);
-        load_global(min(c_begin + 2, c_last), stA);
-        __syncthreads();
-        int c = c_begin;
-        for (; c + 1 < c_end; c += 2) {
-            step(c, 0, stB);        // stores chunk c+1 (stB), refills stB with c+3
-            step(c + 1, 1, stA);    // stores chunk c+2 (stA), refills stA with c+4
-        }
-        if (c < c_end) step(c, 0, stB);
-    }
-
+    const int wn = wave & 3;
+    const int wm = wave >> 2;
     // Accumulator element r of block (m, n) in lane l is token
     // (wm*MBW + m)*32 + 8*(r/4) + 4*(l/32) + r%4 and expert
     // wn*E/4 + n*32 + l%32.
@@ -387,6 +261,163 @@ __global__ __launch_bounds__(64 * NW) void gate_gemm_kernel(GateArgs a)
             select_token<V>(lg, bias_r, lane, a, t, Ls + row * S::LROW);
         }
     }
+}
+
+template <int E, int MB, int NW, int MODE>
+__global__ __launch_bounds__(64 * NW) void gate_gemm_kernel(GateArgs a)
+{
+    using S = Shape<E, MB, NW>;
+    constexpr int NT = S::NT;
+    __shared__ __attribute__((aligned(16))) float smem[S::SMEM];
+    float *const Ws = smem;                    // [2][E][KPAD]
+    float *const Xs = smem + 2 * E * KPAD;     // [2][BM][KPAD]
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wn = wave & 3;            // expert quarter of this wave
+    const int wm = wave >> 2;           // token split of this wave
+    const int t0 = blockIdx.x * S::BM;
+    const int d = a.d;
+    const int c_begin = blockIdx.y * a.chunks_per_split;
+    const int c_end = min(c_begin + a.chunks_per_split, a.chunks_total);
+
+    // ---- global -> register staging.  Thread tid loads W rows
+    // (tid/8) + (NT/8) i, 4 floats at column (tid%8)*4, and x row tid/XT, KC/XT
+    // bfloat16 at column (tid%XT)*(KC/XT).  The steady-state loop has no
+    // branches: columns past d (last chunk only) read a clamped in-range
+    // address, and their x values are zeroed when written to LDS, so the
+    // (finite) W values there multiply zero; rows past T read row T-1 and
+    // their logits are dropped.
+    constexpr int WLOADS = E * 8 / NT;
+    constexpr int XT = NT / S::BM;          // threads per x row: 4 or 8
+    constexpr int XE = KC / XT;             // bfloat16 per thread: 8 or 4
+    typedef unsigned int xvec __attribute__((ext_vector_type(XE / 2)));
+    struct Stage {
+        f32x4 w[WLOADS];
+        xvec x;
+    };
+    const int w_row = tid >> 3;
+    const int w_col = (tid & 7) * 4;
+    const int x_row = tid / XT;
+    const int x_col = (tid % XT) * XE;
+    const int x_t = min(t0 + x_row, a.T - 1);
+    const float *const Wp = a.W + (size_t)w_row * d;
+    const uint16_t *const Xp = a.x + (size_t)x_t * d;
+
+    auto load_global = [&](int c, Stage &st) {
+        const int k0 = c * KC;
+        const int wc = min(k0 + w_col, d - 4);
+        const int xc = min(k0 + x_col, d - XE);
+#pragma unroll
+        for (int i = 0; i < WLOADS; ++i)
+            st.w[i] = *(const f32x4 *)(Wp + (size_t)i * (NT / 8) * d + wc);
+        st.x = *(const xvec *)(Xp + xc);
+    };
+    auto store_lds = [&](int c, int buf, const Stage &st) {
+        const int k0 = c * KC;
+        const bool xk = k0 + x_col < d;
+        float *wb = Ws + buf * E * KPAD;
+#pragma unroll
+        for (int i = 0; i < WLOADS; ++i)
+            *(f32x4 *)(wb + (w_row + (NT / 8) * i) * KPAD + w_col) = st.w[i];
+        float *xb = Xs + buf * S::BM * KPAD + x_row * KPAD + x_col;
+#pragma unroll
+        for (int h = 0; h < XE / 4; ++h) {
+            const unsigned u0 = xk ? st.x[2 * h] : 0u;
+            const unsigned u1 = xk ? st.x[2 * h + 1] : 0u;
+            *(f32x4 *)(xb + 4 * h) = f32x4{bf16_lo(u0), bf16_hi(u0), bf16_lo(u1), bf16_hi(u1)};
+        }
+    };
+
+    // ---- MFMA main loop.  For a group of 8 k-columns, lane l reads 4
+    // consecutive k of row (l%32) at offset 4*(l/32); MFMA j pairs column j
+    // (lanes 0-31) with column 4+j (lanes 32-63) for A and B alike.
+    f32x16 acc[S::MBW][S::NB];
+#pragma unroll
+    for (int m = 0; m < S::MBW; ++m)
+#pragma unroll
+        for (int n = 0; n < S::NB; ++n)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[m][n][r] = 0.0f;
+
+    const int f_row = lane & 31;
+    const int f_k = (lane >> 5) * 4;
+    // Operand fragments of one 8-column group, and their MFMAs.
+    struct Frag {
+        f32x4 a[S::MBW];
+        f32x4 b[S::NB];
+    };
+    auto read_frag = [&](int buf, int c8, Frag &f) {
+        const float *xb = Xs + buf * S::BM * KPAD + wm * S::MBW * 32 * KPAD;
+        const float *wb = Ws + buf * E * KPAD + wn * S::WCOLS * KPAD;
+#pragma unroll
+        for (int m = 0; m < S::MBW; ++m)
+            f.a[m] = *(const f32x4 *)(xb + (m * 32 + f_row) * KPAD + c8 * 8 + f_k);
+#pragma unroll
+        for (int n = 0; n < S::NB; ++n)
+            f.b[n] = *(const f32x4 *)(wb + (n * 32 + f_row) * KPAD + c8 * 8 + f_k);
+    };
+    auto mma = [&](const Frag &f) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int m = 0; m < S::MBW; ++m)
+#pragma unroll
+                for (int n = 0; n < S::NB; ++n)
+                    acc[m][n] = __builtin_amdgcn_mfma_f32_32x32x2f32(f.a[m][j], f.b[n][j],
+                                                                     acc[m][n], 0, 0, 0);
+    };
+    static_assert(KC == 32, "the step below is written for four 8-column groups");
+
+    // Pipeline over KC-column chunks.  While chunk c feeds the matrix cores
+    // from one LDS buffer, chunks c+1 and c+2 wait in two register stages.
+    // After the first 8-column group of chunk c, chunk c+1 is written to the
+    // other LDS buffer and its register stage is refilled with chunk c+3, so
+    // every global load has two chunks of MFMA work to land in.  The one
+    // barrier per chunk comes once the last fragments of chunk c are in
+    // registers: the MFMAs of that last group then cover the LDS latency of
+    // the first fragments of chunk c+1.  The stages alternate, so the loop
+    // handles chunks in pairs (static indices).  Past the last chunk, loads
+    // and stores repeat the last chunk (never read) instead of branching.
+    if (c_begin < c_end) {
+        const int c_last = c_end - 1;
+        Stage stA, stB;
+        Frag f, g;
+        auto step = [&](int c, int buf, Stage &st) {
+            // f holds group 0 of chunk c
+            read_frag(buf, 1, g);
+            mma(f);
+            store_lds(min(c + 1, c_last), buf ^ 1, st);
+            load_global(min(c + 3, c_last), st);
+            read_frag(buf, 2, f);
+            mma(g);
+            read_frag(buf, 3, g);
+            mma(f);
+            // keep the last group's MFMAs after the barrier (the scheduler
+            // would otherwise hoist them and expose the LDS latency below)
+            __builtin_amdgcn_sched_barrier(0);
+            __syncthreads();
+            __builtin_amdgcn_sched_barrier(0);
+            read_frag(buf ^ 1, 0, f);   // group 0 of chunk c+1
+            mma(g);
+        };
+        load_global(c_begin, stA);
+        load_global(min(c_begin + 1, c_last), stB);
+        store_lds(c_begin, 0, stA);
+        load_global(min(c_begin + 2, c_last), stA);
+        __syncthreads();
+        read_frag(0, 0, f);
+        int c = c_begin;
+        for (; c + 1 < c_end; c += 2) {
+            step(c, 0, stB);        // stores chunk c+1 (stB), refills stB with c+3
+            step(c + 1, 1, stA);    // stores chunk c+2 (stA), refills stA with c+4
+        }
+        if (c < c_end) step(c, 0, stB);
+        __syncthreads();   // every wave is done with the staging buffers
+    }
+
+    finish_tile<E, MB, NW, MODE>(a, acc, smem, t0, wave, lane);
 }
 
 // Adds the n_split partial logits of one token (fixed order s = 0, 1, ...)
