@@ -11,12 +11,14 @@
 // Four launches, none of them with order-dependent atomics:
 //   count   one block per 256 tokens; each wave ORs a 64-bit lane mask per
 //           expert in LDS (bit l = token l of the wave routes there), so the
-//           block's count of expert e is the popcount of its 4 masks.
-//   scan    one block: per-expert totals, their exclusive prefix (offsets)
-//           and the base position of every (block, expert) run.
-//   scatter recomputes the masks; the rank of a pair inside its block is
-//           the popcount of lower lanes' bits plus earlier waves' counts,
-//           which is exactly ascending token order.
+//           block's count of expert e is the popcount of its 4 masks;
+//           written expert-major, counts[e][b].
+//   scan    one block per expert: exclusive prefix of counts[e][.] over
+//           the token blocks, and the expert's total.
+//   scatter each block takes the exclusive prefix of the E totals (the
+//           expert offsets), recomputes its masks, and places every pair at
+//           offset[e] + prefix[e][b] + (popcount of lower lanes' bits plus
+//           earlier waves' counts) -- exactly ascending token order.
 //   gather  one block per token: read the row once, write it to its K
 //           destinations with non-temporal 16-byte stores.
 #include "siggate_internal.h"
@@ -29,7 +31,7 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int BT = DISPATCH_BLOCK_TOKENS;
 constexpr int WAVES = BT / 64;
-constexpr int SCAN_THREADS = 1024;
+constexpr int SCAN_THREADS = 256;
 
 // Loads the K expert ids of token t into e[] (-1 past K or for t >= T).
 __device__ __forceinline__ void load_row(const DispatchArgs &a, int t, int (&e)[MAX_TOPK])
@@ -75,75 +77,84 @@ __global__ __launch_bounds__(BT) void dispatch_count_kernel(DispatchArgs a)
         int c = 0;
 #pragma unroll
         for (int w = 0; w < WAVES; ++w) c += __popcll(masks[w][x]);
-        a.block_counts[(size_t)blockIdx.x * a.E + x] = c;
+        a.block_counts[(size_t)x * a.n_blocks + blockIdx.x] = c;
     }
 }
 
+// Block e: exclusive prefix over token blocks of counts[e][.] (in place
+// into block_base[e][.]) and tokens_per_expert[e].
 __global__ __launch_bounds__(SCAN_THREADS) void dispatch_scan_kernel(DispatchArgs a)
 {
-    __shared__ int seg_sum[SCAN_THREADS];
-    __shared__ int excl[MAX_EXPERTS];
     __shared__ int wave_tot[SCAN_THREADS / 64];
-    const int E = a.E, NB = a.n_blocks, tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
-
-    // Thread (seg, e) sums block_counts[b, e] over its slice of blocks.
-    const int segs = SCAN_THREADS / E;
-    const int seg = tid / E, e = tid - seg * E;
-    const bool active = seg < segs;
-    const int per = (NB + segs - 1) / segs;
-    const int b0 = active ? min(seg * per, NB) : 0;
-    const int b1 = active ? min(b0 + per, NB) : 0;
-    int sum = 0;
-    for (int b = b0; b < b1; ++b) sum += a.block_counts[(size_t)b * E + e];
-    if (active) seg_sum[seg * E + e] = sum;
-    __syncthreads();
-
-    // Per-expert total and its exclusive prefix over experts.
-    int tot = 0;
-    if (tid < E)
-        for (int s = 0; s < segs; ++s) tot += seg_sum[s * E + tid];
-    int inc = tot;
-    for (int off = 1; off < 64; off <<= 1) {
-        const int y = __shfl_up(inc, off);
-        if (lane >= off) inc += y;
-    }
-    if (lane == 63) wave_tot[wave] = inc;
-    __syncthreads();
-    int ex = inc - tot;
-    for (int w = 0; w < wave; ++w) ex += wave_tot[w];
-    if (tid < E) {
-        excl[tid] = ex;
-        a.tokens_per_expert[tid] = tot;
-        if (a.offsets) a.offsets[tid] = ex;
-        if (tid == E - 1 && a.offsets) a.offsets[E] = ex + tot;
-    }
-    __syncthreads();
-
-    // Base position of the run of (block b, expert e).
-    if (active) {
-        int run = excl[e];
-        for (int s = 0; s < seg; ++s) run += seg_sum[s * E + e];
-        for (int b = b0; b < b1; ++b) {
-            const size_t i = (size_t)b * E + e;
-            const int c = a.block_counts[i];
-            a.block_base[i] = run;
-            run += c;
+    const int e = blockIdx.x;
+    const int NB = a.n_blocks;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int32_t *cnt = a.block_counts + (size_t)e * NB;
+    int32_t *base = a.block_base + (size_t)e * NB;
+    int carry = 0;
+    for (int b0 = 0; b0 < NB; b0 += SCAN_THREADS) {
+        const int b = b0 + tid;
+        const int c = b < NB ? cnt[b] : 0;
+        int inc = c;
+        for (int off = 1; off < 64; off <<= 1) {
+            const int y = __shfl_up(inc, off);
+            if (lane >= off) inc += y;
         }
+        if (lane == 63) wave_tot[wave] = inc;
+        __syncthreads();
+        int before = 0, all = 0;
+        for (int w = 0; w < SCAN_THREADS / 64; ++w) {
+            before += w < wave ? wave_tot[w] : 0;
+            all += wave_tot[w];
+        }
+        if (b < NB) base[b] = carry + before + inc - c;
+        carry += all;
+        __syncthreads();
     }
+    if (tid == 0) a.tokens_per_expert[e] = carry;
 }
 
 __global__ __launch_bounds__(BT) void dispatch_scatter_kernel(DispatchArgs a)
 {
     __shared__ unsigned long long masks[WAVES][MAX_EXPERTS];
+    __shared__ int offset[MAX_EXPERTS];
+    __shared__ int wave_tot[WAVES];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int t = blockIdx.x * BT + threadIdx.x;
+
+    // Expert offsets: exclusive prefix of tokens_per_expert over experts.
+    for (int e0 = 0; e0 < a.E; e0 += BT) {
+        const int x = e0 + threadIdx.x;
+        const int c = x < a.E ? a.tokens_per_expert[x] : 0;
+        int inc = c;
+        for (int off = 1; off < 64; off <<= 1) {
+            const int y = __shfl_up(inc, off);
+            if (lane >= off) inc += y;
+        }
+        if (lane == 63) wave_tot[wave] = inc;
+        __syncthreads();
+        int before = e0 > 0 ? offset[e0 - 1] : 0;   // inclusive total so far
+        for (int w = 0; w < wave; ++w) before += wave_tot[w];
+        __syncthreads();
+        if (x < a.E) offset[x] = before + inc;        // inclusive for now
+        __syncthreads();
+    }
+    for (int x = threadIdx.x; x < a.E; x += BT) {
+        const int excl = offset[x] - a.tokens_per_expert[x];
+        if (blockIdx.x == 0 && a.offsets) {
+            a.offsets[x] = excl;
+            if (x == a.E - 1) a.offsets[a.E] = offset[x];
+        }
+    }
+    __syncthreads();
+    for (int x = threadIdx.x; x < a.E; x += BT)
+        offset[x] -= a.tokens_per_expert[x];   // now exclusive
+
     int e[MAX_TOPK];
     load_row(a, t, e);
-    build_masks(a, masks, e, lane, wave);
+    build_masks(a, masks, e, lane, wave);   // its barriers also publish offset[]
     if (t >= a.T) return;
     const unsigned long long lower = (1ull << lane) - 1ull;
-    const int32_t *base = a.block_base + (size_t)blockIdx.x * a.E;
 #pragma unroll
     for (int k = 0; k < MAX_TOPK; ++k) {
         if (k >= a.top_k) break;
@@ -153,7 +164,8 @@ __global__ __launch_bounds__(BT) void dispatch_scatter_kernel(DispatchArgs a)
             a.dest[p] = -1;
             continue;
         }
-        int pos = base[x] + __popcll(masks[wave][x] & lower);
+        int pos = offset[x] + a.block_base[(size_t)x * a.n_blocks + blockIdx.x] +
+                  __popcll(masks[wave][x] & lower);
         for (int w = 0; w < wave; ++w) pos += __popcll(masks[w][x]);
         a.perm[pos] = (int)p;
         a.dest[p] = pos;
@@ -181,6 +193,15 @@ __global__ __launch_bounds__(256) void dispatch_gather_kernel(DispatchArgs a)
     }
 }
 
+// T == 0: every count and offset is zero.
+__global__ __launch_bounds__(BT) void dispatch_zero_kernel(DispatchArgs a)
+{
+    for (int x = threadIdx.x; x <= a.E; x += BT) {
+        if (x < a.E) a.tokens_per_expert[x] = 0;
+        if (a.offsets) a.offsets[x] = 0;
+    }
+}
+
 }  // namespace
 
 static size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
@@ -195,13 +216,14 @@ size_t dispatch_workspace_bytes(int T, int E, int top_k, bool need_dest)
 
 hipError_t launch_dispatch(const DispatchArgs &a, hipStream_t stream)
 {
-    if (a.n_blocks > 0)
-        hipLaunchKernelGGL(dispatch_count_kernel, dim3(a.n_blocks), dim3(BT), 0, stream, a);
-    hipLaunchKernelGGL(dispatch_scan_kernel, dim3(1), dim3(SCAN_THREADS), 0, stream, a);
-    if (a.n_blocks > 0) {
-        hipLaunchKernelGGL(dispatch_scatter_kernel, dim3(a.n_blocks), dim3(BT), 0, stream, a);
-        hipLaunchKernelGGL(dispatch_gather_kernel, dim3(a.T), dim3(256), 0, stream, a);
+    if (a.n_blocks == 0) {
+        hipLaunchKernelGGL(dispatch_zero_kernel, dim3(1), dim3(BT), 0, stream, a);
+        return hipGetLastError();
     }
+    hipLaunchKernelGGL(dispatch_count_kernel, dim3(a.n_blocks), dim3(BT), 0, stream, a);
+    hipLaunchKernelGGL(dispatch_scan_kernel, dim3(a.E), dim3(SCAN_THREADS), 0, stream, a);
+    hipLaunchKernelGGL(dispatch_scatter_kernel, dim3(a.n_blocks), dim3(BT), 0, stream, a);
+    hipLaunchKernelGGL(dispatch_gather_kernel, dim3(a.T), dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 
