@@ -35,12 +35,15 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 constexpr int RED_NT = 256;     // threads per workgroup of the split-k reduction
 constexpr int KPAD = KC + 4;    // padded LDS row in floats: rows start 4 banks apart
 
-// Workgroup of NW waves: 4 expert quarters x NW/4 token splits.
+// Workgroup of NW waves: 4 expert quarters x WM token splits x KS k-splits.
+// A k-split wave pair shares a tile and processes alternate halves of every
+// chunk; their accumulators are added in a fixed order at the end.
 template <int E, int MB, int NW>
 struct Shape {
     static constexpr int NT = 64 * NW;          // threads per workgroup
     static constexpr int BM = 32 * MB;          // tokens per workgroup
-    static constexpr int WM = NW / 4;           // token splits
+    static constexpr int WM = MB < NW / 4 ? MB : NW / 4;   // token splits
+    static constexpr int KS = NW / 4 / WM;      // k-splits (1 or 2)
     static constexpr int MBW = MB / WM;         // 32-token MFMA blocks per wave
     static constexpr int NB = E / 128;          // 32-expert MFMA blocks per wave
     static constexpr int WCOLS = E / 4;         // experts per wave
@@ -50,9 +53,14 @@ struct Shape {
     static constexpr int EPI = BM * LROW;
     static constexpr int SMEM = STAGE > EPI ? STAGE : EPI;
     static_assert(E % 128 == 0, "E must be a multiple of 128");
-    static_assert(NW % 4 == 0 && MB % WM == 0, "waves must tile the workgroup");
-    static_assert(KC * BM / NT >= 4, "each thread stages at least 4 bfloat16 of x");
+    static_assert(NW % 4 == 0 && MB % WM == 0 && (KS == 1 || KS == 2), "waves must tile the workgroup");
+    static_assert(KC * BM / NT >= 2, "each thread stages at least 2 bfloat16 of x");
+    static_assert(KS == 1 || 4 * MBW * NB * 16 * 64 <= SMEM, "k-split reduction fits in LDS");
 };
+
+// N packed bfloat16 pairs (one 32-bit word each)
+template <int N> struct XVec { typedef unsigned int type __attribute__((ext_vector_type(N))); };
+template <> struct XVec<1> { typedef unsigned int type; };
 
 __device__ __forceinline__ float bf16_lo(unsigned w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(unsigned w) { return __uint_as_float(w & 0xffff0000u); }
@@ -207,11 +215,10 @@ template <int E, int MB, int NW, int MODE>
 __device__ __forceinline__ void finish_tile(const GateArgs &a,
                                             f32x16 (&acc)[Shape<E, MB, NW>::MBW][Shape<E, MB, NW>::NB],
                                             float *smem, const int t0, const int wave,
-                                            const int lane)
+                                            const int lane, const int wm, const bool has_acc)
 {
     using S = Shape<E, MB, NW>;
     const int wn = wave & 3;
-    const int wm = wave >> 2;
     // Accumulator element r of block (m, n) in lane l is token
     // (wm*MBW + m)*32 + 8*(r/4) + 4*(l/32) + r%4 and expert
     // wn*E/4 + n*32 + l%32.
@@ -227,21 +234,23 @@ __device__ __forceinline__ void finish_tile(const GateArgs &a,
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int t = t0 + m * 32 + 8 * (r >> 2) + r_base + (r & 3);
-                    if (t < a.T) out[(size_t)t * E + e_base + n * 32] = acc[m][n][r];
+                    if (has_acc && t < a.T) out[(size_t)t * E + e_base + n * 32] = acc[m][n][r];
                 }
     } else {
         // Scores go to LDS (never to HBM); each wave then selects for BM/NW
         // tokens.
         float *const Ls = smem;   // [BM][LROW]
+        if (has_acc) {
 #pragma unroll
-        for (int m = 0; m < S::MBW; ++m)
+            for (int m = 0; m < S::MBW; ++m)
 #pragma unroll
-            for (int n = 0; n < S::NB; ++n)
+                for (int n = 0; n < S::NB; ++n)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int row = m * 32 + 8 * (r >> 2) + r_base + (r & 3);
-                    Ls[row * S::LROW + e_base + n * 32] = acc[m][n][r];
-                }
+                    for (int r = 0; r < 16; ++r) {
+                        const int row = m * 32 + 8 * (r >> 2) + r_base + (r & 3);
+                        Ls[row * S::LROW + e_base + n * 32] = acc[m][n][r];
+                    }
+        }
         __syncthreads();
 
         constexpr int V = S::V;
@@ -275,8 +284,9 @@ __global__ __launch_bounds__(64 * NW) void gate_gemm_kernel(GateArgs a)
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int wn = wave & 3;            // expert quarter of this wave
-    const int wm = wave >> 2;           // token split of this wave
+    const int wn = wave & 3;                    // expert quarter of this wave
+    const int wm = (wave >> 2) % S::WM;         // token split of this wave
+    const int wk = (wave >> 2) / S::WM;         // k-split of this wave
     const int t0 = blockIdx.x * S::BM;
     const int d = a.d;
     const int c_begin = blockIdx.y * a.chunks_per_split;
@@ -290,9 +300,9 @@ __global__ __launch_bounds__(64 * NW) void gate_gemm_kernel(GateArgs a)
     // (finite) W values there multiply zero; rows past T read row T-1 and
     // their logits are dropped.
     constexpr int WLOADS = E * 8 / NT;
-    constexpr int XT = NT / S::BM;          // threads per x row: 4 or 8
-    constexpr int XE = KC / XT;             // bfloat16 per thread: 8 or 4
-    typedef unsigned int xvec __attribute__((ext_vector_type(XE / 2)));
+    constexpr int XT = NT / S::BM;          // threads per x row: 4, 8 or 16
+    constexpr int XE = KC / XT;             // bfloat16 per thread: 8, 4 or 2
+    typedef typename XVec<XE / 2>::type xvec;
     struct Stage {
         f32x4 w[WLOADS];
         xvec x;
@@ -322,11 +332,17 @@ __global__ __launch_bounds__(64 * NW) void gate_gemm_kernel(GateArgs a)
         for (int i = 0; i < WLOADS; ++i)
             *(f32x4 *)(wb + (w_row + (NT / 8) * i) * KPAD + w_col) = st.w[i];
         float *xb = Xs + buf * S::BM * KPAD + x_row * KPAD + x_col;
+        if constexpr (XE >= 4) {
 #pragma unroll
-        for (int h = 0; h < XE / 4; ++h) {
-            const unsigned u0 = xk ? st.x[2 * h] : 0u;
-            const unsigned u1 = xk ? st.x[2 * h + 1] : 0u;
-            *(f32x4 *)(xb + 4 * h) = f32x4{bf16_lo(u0), bf16_hi(u0), bf16_lo(u1), bf16_hi(u1)};
+            for (int h = 0; h < XE / 4; ++h) {
+                const unsigned u0 = xk ? st.x[2 * h] : 0u;
+                const unsigned u1 = xk ? st.x[2 * h + 1] : 0u;
+                *(f32x4 *)(xb + 4 * h) = f32x4{bf16_lo(u0), bf16_hi(u0), bf16_lo(u1), bf16_hi(u1)};
+            }
+        } else {
+            typedef float f32x2 __attribute__((ext_vector_type(2)));
+            const unsigned u0 = xk ? st.x : 0u;
+            *(f32x2 *)xb = f32x2{bf16_lo(u0), bf16_hi(u0)};
         }
     };
 
@@ -384,22 +400,26 @@ __global__ __launch_bounds__(64 * NW) void gate_gemm_kernel(GateArgs a)
         const int c_last = c_end - 1;
         Stage stA, stB;
         Frag f, g;
+        // this wave's 8-column groups of every chunk: g0 .. g0 + 4/KS - 1
+        const int g0 = wk * (4 / S::KS);
         auto step = [&](int c, int buf, Stage &st) {
-            // f holds group 0 of chunk c
-            read_frag(buf, 1, g);
+            // f holds group g0 of chunk c
+            read_frag(buf, g0 + 1, g);
             mma(f);
             store_lds(min(c + 1, c_last), buf ^ 1, st);
             load_global(min(c + 3, c_last), st);
-            read_frag(buf, 2, f);
-            mma(g);
-            read_frag(buf, 3, g);
-            mma(f);
+            if constexpr (S::KS == 1) {
+                read_frag(buf, 2, f);
+                mma(g);
+                read_frag(buf, 3, g);
+                mma(f);
+            }
             // keep the last group's MFMAs after the barrier (the scheduler
             // would otherwise hoist them and expose the LDS latency below)
             __builtin_amdgcn_sched_barrier(0);
             __syncthreads();
             __builtin_amdgcn_sched_barrier(0);
-            read_frag(buf ^ 1, 0, f);   // group 0 of chunk c+1
+            read_frag(buf ^ 1, g0, f);   // first group of chunk c+1
             mma(g);
         };
         load_global(c_begin, stA);
@@ -407,7 +427,7 @@ __global__ __launch_bounds__(64 * NW) void gate_gemm_kernel(GateArgs a)
         store_lds(c_begin, 0, stA);
         load_global(min(c_begin + 2, c_last), stA);
         __syncthreads();
-        read_frag(0, 0, f);
+        read_frag(0, g0, f);
         int c = c_begin;
         for (; c + 1 < c_end; c += 2) {
             step(c, 0, stB);        // stores chunk c+1 (stB), refills stB with c+3
@@ -417,27 +437,68 @@ __global__ __launch_bounds__(64 * NW) void gate_gemm_kernel(GateArgs a)
         __syncthreads();   // every wave is done with the staging buffers
     }
 
-    finish_tile<E, MB, NW, MODE>(a, acc, smem, t0, wave, lane);
+    if constexpr (S::KS == 2) {
+        // k-split pair: the second wave hands its sums to the first, which
+        // adds them after its own (fixed order)
+        constexpr int REGS = S::MBW * S::NB * 16;
+        float *red = smem + wn * REGS * 64 + lane;
+        if (wk == 1) {
+#pragma unroll
+            for (int m = 0; m < S::MBW; ++m)
+#pragma unroll
+                for (int n = 0; n < S::NB; ++n)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) red[((m * S::NB + n) * 16 + r) * 64] = acc[m][n][r];
+        }
+        __syncthreads();
+        if (wk == 0) {
+#pragma unroll
+            for (int m = 0; m < S::MBW; ++m)
+#pragma unroll
+                for (int n = 0; n < S::NB; ++n)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) acc[m][n][r] += red[((m * S::NB + n) * 16 + r) * 64];
+        }
+        __syncthreads();
+    }
+
+    finish_tile<E, MB, NW, MODE>(a, acc, smem, t0, wave, lane, wm, wk == 0);
 }
 
-// Adds the n_split partial logits of one token (fixed order s = 0, 1, ...)
-// and writes the logits or runs the selection.  One wave per token.
+// Adds the n_split partial logits of one token in a fixed order -- wave w
+// sums its contiguous quarter of the slices, then wave 0 adds the four
+// quarter sums in wave order -- and writes the logits or runs the selection.
+// One workgroup per token.
 template <int E, int MODE>
 __global__ __launch_bounds__(RED_NT) void gate_reduce_kernel(GateArgs a)
 {
     constexpr int V = E / 64;
-    __shared__ float scratch[RED_NT / 64][3 * MAX_TOPK];
+    constexpr int NWR = RED_NT / 64;
+    __shared__ float part[NWR][E];
+    __shared__ float scratch[3 * MAX_TOPK];
     const int lane = threadIdx.x & 63;
-    const int t = blockIdx.x * (RED_NT / 64) + (threadIdx.x >> 6);
-    if (t >= a.T) return;
+    const int wave = threadIdx.x >> 6;
+    const int t = blockIdx.x;
+    const int per = (a.n_split + NWR - 1) / NWR;
+    const int s0 = min(wave * per, a.n_split);
+    const int s1 = min(s0 + per, a.n_split);
     float lg[V];
 #pragma unroll
     for (int j = 0; j < V; ++j) lg[j] = 0.0f;
-    for (int s = 0; s < a.n_split; ++s) {
+#pragma unroll 4
+    for (int s = s0; s < s1; ++s) {
         const float *p = a.partial + ((size_t)s * a.T + t) * E + lane * V;
 #pragma unroll
         for (int j = 0; j < V; ++j) lg[j] += p[j];
     }
+#pragma unroll
+    for (int j = 0; j < V; ++j) part[wave][lane * V + j] = lg[j];
+    __syncthreads();
+    if (wave != 0) return;
+#pragma unroll
+    for (int w = 1; w < NWR; ++w)
+#pragma unroll
+        for (int j = 0; j < V; ++j) lg[j] += part[w][lane * V + j];
     if constexpr (MODE == MODE_LOGITS) {
 #pragma unroll
         for (int j = 0; j < V; ++j) a.logits[(size_t)t * E + lane * V + j] = lg[j];
@@ -445,7 +506,7 @@ __global__ __launch_bounds__(RED_NT) void gate_reduce_kernel(GateArgs a)
         float bias_r[V];
 #pragma unroll
         for (int j = 0; j < V; ++j) bias_r[j] = a.bias[lane * V + j];
-        select_token<V>(lg, bias_r, lane, a, t, scratch[threadIdx.x >> 6]);
+        select_token<V>(lg, bias_r, lane, a, t, scratch);
     }
 }
 
@@ -464,16 +525,17 @@ hipError_t launch_for_e(const GateArgs &a, const GatePlan &p, GateMode final_mod
             else
                 hipLaunchKernelGGL((gate_gemm_kernel<E, 2, 8, MODE_LOGITS>), grid, block, 0, stream, a);
         } else {
-            const dim3 block(64 * 4);
+            // 32 tokens: 8 waves, the two of a pair split every chunk's k
+            const dim3 block(64 * 8);
             if (final_mode == MODE_SELECT)
-                hipLaunchKernelGGL((gate_gemm_kernel<E, 1, 4, MODE_SELECT>), grid, block, 0, stream, a);
+                hipLaunchKernelGGL((gate_gemm_kernel<E, 1, 8, MODE_SELECT>), grid, block, 0, stream, a);
             else
-                hipLaunchKernelGGL((gate_gemm_kernel<E, 1, 4, MODE_LOGITS>), grid, block, 0, stream, a);
+                hipLaunchKernelGGL((gate_gemm_kernel<E, 1, 8, MODE_LOGITS>), grid, block, 0, stream, a);
         }
     } else {
         const dim3 grid((a.T + 31) / 32, p.n_split);
-        hipLaunchKernelGGL((gate_gemm_kernel<E, 1, 4, MODE_PARTIAL>), grid, dim3(256), 0, stream, a);
-        const dim3 rgrid((a.T + 3) / 4);
+        hipLaunchKernelGGL((gate_gemm_kernel<E, 1, 8, MODE_PARTIAL>), grid, dim3(64 * 8), 0, stream, a);
+        const dim3 rgrid(a.T);
         if (final_mode == MODE_SELECT)
             hipLaunchKernelGGL((gate_reduce_kernel<E, MODE_SELECT>), rgrid, dim3(RED_NT), 0, stream, a);
         else
