@@ -86,13 +86,13 @@ class Oracle:
                                       i64, i64, i64, P(dbl)]
         lib.oracle_select.restype = i32
         lib.oracle_select.argtypes = [P(dbl), P(ctypes.c_float), i64, i64,
-                                      i32, i32, i32, dbl, i32, P(dbl),
-                                      P(ctypes.c_int32), P(dbl)]
+                                      i32, i32, i32, dbl, i32, i32, i32, i32,
+                                      dbl, P(dbl), P(ctypes.c_int32), P(dbl)]
         lib.oracle_gate.restype = i32
         lib.oracle_gate.argtypes = [P(ctypes.c_uint16), P(ctypes.c_float),
                                     P(ctypes.c_float), i64, i64, i64, i32,
-                                    i32, i32, dbl, i32, P(dbl),
-                                    P(ctypes.c_int32), P(dbl)]
+                                    i32, i32, dbl, i32, i32, i32, i32, dbl,
+                                    P(dbl), P(ctypes.c_int32), P(dbl)]
         lib.oracle_dispatch.restype = i32
         lib.oracle_dispatch.argtypes = [P(ctypes.c_int32), i64, i32, i64,
                                         P(ctypes.c_int32), P(ctypes.c_int32),
@@ -101,6 +101,10 @@ class Oracle:
         lib.oracle_gather_rows.argtypes = [P(ctypes.c_uint16), i64, i64, i32,
                                            P(ctypes.c_int32), i64,
                                            P(ctypes.c_uint16)]
+        lib.oracle_combine.restype = i32
+        lib.oracle_combine.argtypes = [P(ctypes.c_uint16), i64, P(dbl),
+                                       P(ctypes.c_int32), i64, i32, i64,
+                                       P(dbl), P(ctypes.c_uint16)]
         self.lib = lib
 
     # -- helpers -----------------------------------------------------------
@@ -120,21 +124,33 @@ class Oracle:
                                T, d, E, _ptr(out, ctypes.c_double))
         return out
 
-    def select(self, logits: np.ndarray, bias: np.ndarray, n_group: int,
-               topk_group: int, top_k: int, route_scale: float,
-               order: int = 0) -> GateResult:
-        """Gate steps after the logits, from float64 logits [T, E]."""
-        L = np.ascontiguousarray(logits, dtype=np.float64)
+    @staticmethod
+    def _bias_ptr(bias, E):
+        if bias is None:
+            return None, ctypes.POINTER(ctypes.c_float)()
         b = np.ascontiguousarray(bias, dtype=np.float32)
-        T, E = L.shape
         if b.shape != (E,):
             raise ValueError("bias must have shape [E]")
+        return b, _ptr(b, ctypes.c_float)
+
+    def select(self, logits: np.ndarray, bias: np.ndarray | None, n_group: int,
+               topk_group: int, top_k: int, route_scale: float,
+               order: int = 0, score_func: int = 0, renorm: int = 0,
+               mask_zero: int = 0, denom_eps: float = 0.0) -> GateResult:
+        """Gate steps after the logits, from float64 logits [T, E].
+        bias=None selects the no-bias variant (group score = group max);
+        score_func 0 sigmoid / 1 softmax; renorm 0 auto / 1 on / 2 off;
+        mask_zero fills dropped groups with 0.0 instead of -inf."""
+        L = np.ascontiguousarray(logits, dtype=np.float64)
+        T, E = L.shape
+        b, bp = self._bias_ptr(bias, E)
         w = np.empty((T, top_k), dtype=np.float64)
         idx = np.empty((T, top_k), dtype=np.int32)
         m = np.empty((T, 2), dtype=np.float64)
-        rc = self.lib.oracle_select(_ptr(L, ctypes.c_double), _ptr(b, ctypes.c_float),
+        rc = self.lib.oracle_select(_ptr(L, ctypes.c_double), bp,
                                     T, E, n_group, topk_group, top_k,
-                                    float(route_scale), order,
+                                    float(route_scale), order, score_func, renorm,
+                                    mask_zero, float(denom_eps),
                                     _ptr(w, ctypes.c_double),
                                     _ptr(idx, ctypes.c_int32),
                                     _ptr(m, ctypes.c_double))
@@ -142,23 +158,26 @@ class Oracle:
             raise ValueError(f"oracle_select rejected the configuration (rc={rc})")
         return GateResult(w, idx, m)
 
-    def gate(self, x_bf16: np.ndarray, W: np.ndarray, bias: np.ndarray,
+    def gate(self, x_bf16: np.ndarray, W: np.ndarray, bias: np.ndarray | None,
              n_group: int, topk_group: int, top_k: int, route_scale: float,
-             order: int = 0) -> GateResult:
-        """Whole gate from bfloat16 bits x [T, d], float32 W [E, d], bias [E]."""
+             order: int = 0, score_func: int = 0, renorm: int = 0,
+             mask_zero: int = 0, denom_eps: float = 0.0) -> GateResult:
+        """Whole gate from bfloat16 bits x [T, d], float32 W [E, d], bias [E]
+        (or None); options as in select()."""
         x = np.ascontiguousarray(x_bf16, dtype=np.uint16)
         W = np.ascontiguousarray(W, dtype=np.float32)
-        b = np.ascontiguousarray(bias, dtype=np.float32)
         T, d = x.shape
         E, d2 = W.shape
-        if d != d2 or b.shape != (E,):
-            raise ValueError("shape mismatch between x, W and bias")
+        if d != d2:
+            raise ValueError("shape mismatch between x and W")
+        b, bp = self._bias_ptr(bias, E)
         w = np.empty((T, top_k), dtype=np.float64)
         idx = np.empty((T, top_k), dtype=np.int32)
         m = np.empty((T, 2), dtype=np.float64)
         rc = self.lib.oracle_gate(_ptr(x, ctypes.c_uint16), _ptr(W, ctypes.c_float),
-                                  _ptr(b, ctypes.c_float), T, d, E, n_group,
+                                  bp, T, d, E, n_group,
                                   topk_group, top_k, float(route_scale), order,
+                                  score_func, renorm, mask_zero, float(denom_eps),
                                   _ptr(w, ctypes.c_double),
                                   _ptr(idx, ctypes.c_int32),
                                   _ptr(m, ctypes.c_double))
@@ -195,6 +214,29 @@ class Oracle:
         if rc != OK:
             raise ValueError("oracle_gather_rows: permutation entry out of range")
         return out
+
+
+    def combine(self, expert_out_bf16: np.ndarray, weights: np.ndarray,
+                dest: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+        """y[t] = sum_k w[t,k] * out[dest[t*K+k]] for expert outputs in
+        dispatch order (bfloat16 bits [n_pos, d]).  Returns (float64 sums
+        [T, d], bfloat16 bits [T, d] of the sums rounded via float32)."""
+        out = np.ascontiguousarray(expert_out_bf16, dtype=np.uint16)
+        w = np.ascontiguousarray(weights, dtype=np.float64)
+        dst = np.ascontiguousarray(dest, dtype=np.int32).ravel()
+        T, K = w.shape
+        n_pos, d = out.shape
+        if dst.shape != (T * K,):
+            raise ValueError("dest must have T*K entries")
+        y64 = np.empty((T, d), dtype=np.float64)
+        y16 = np.empty((T, d), dtype=np.uint16)
+        rc = self.lib.oracle_combine(_ptr(out, ctypes.c_uint16), n_pos,
+                                     _ptr(w, ctypes.c_double), _ptr(dst, ctypes.c_int32),
+                                     T, K, d, _ptr(y64, ctypes.c_double),
+                                     _ptr(y16, ctypes.c_uint16))
+        if rc != OK:
+            raise ValueError("oracle_combine: dest entry out of range")
+        return y64, y16
 
 
 _DEFAULT: Oracle | None = None

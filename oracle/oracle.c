@@ -23,9 +23,22 @@
  *     8. renormalise over the K winners, multiply by route_scale
  *        (eq. for g'/g; Normalize-weights equation G_i)
  *
+ *   options (DeepSeek-V3.2-Exp · Normalize weights, "Code"; Kimi K2 ·
+ *   Normalize weights, "Code"):
+ *     - score function softmax over the E logits instead of sigmoid;
+ *     - no bias: choice score = affinity, group score = group maximum;
+ *     - renormalisation: by default only for sigmoid (DeepSeek-V3.2-Exp),
+ *       or forced on / off (Kimi K2 gates it on a config flag);
+ *     - dropped groups filled with 0.0 instead of -inf, and an epsilon added
+ *       to the renormalisation denominator (both as the Kimi K2 gate does).
+ *
  *   dispatch (Kimi K2 · Add shared output, "Code": moe_infer, first lines)
  *     per-expert token counts, expert-major argsort of the flat (token, slot)
  *     pairs, and the row gather x[perm // K].
+ *
+ *   combine (Kimi K2 · Add shared output, "Code": moe_infer, last lines)
+ *     un-permute the expert outputs and sum each token's K rows weighted by
+ *     its gate weights: y[t] = sum_k w[t,k] * out[dest[t*K + k]].
  *
  * Readings taken where the pages leave a choice open:
  *   - arithmetic is float64 throughout (the pages use float32);
@@ -114,24 +127,44 @@ static int precedes(double va, int64_t a, double vb, int64_t b)
     return a < b;
 }
 
+/* Options beyond the default DeepSeek-V3 / Kimi-K2 gate. */
+typedef struct {
+    int score_func;    /* 0 sigmoid, 1 softmax over the E logits           */
+    int renorm;        /* 0 auto (sigmoid: yes, softmax: no), 1 yes, 2 no  */
+    int mask_zero;     /* dropped groups: 0 -> -inf, 1 -> 0.0              */
+    double denom_eps;  /* added to the renormalisation denominator         */
+} gate_opts;
+
 /* Steps 2-8 for one token, from its E logits.
- *   work: scratch of 3*E + 2*G doubles/ints (caller-provided)
+ *   bias: [E] or NULL (no bias: choice score = affinity, group score =
+ *         group maximum)
+ *   scratch: s, v, mv of E doubles; keep, gs of G; chosen of E; sel of K
  *   out_w[K], out_i[K]: weights and expert ids
- *   margin[2]: {v(K) - v(K+1) among the candidates,
- *               gs(KG) - gs(KG+1) among the groups}; +inf when undefined. */
+ *   margin[2]: {K-th minus (K+1)-th masked choice score,
+ *               KG-th minus (KG+1)-th group score}; +inf when undefined. */
 static void select_token(const double *L, const float *bias, int64_t E, int G,
                          int KG, int K, double route_scale, int order,
-                         double *s, double *v, int *keep, double *gs,
-                         int *chosen, int64_t *sel, double *out_w,
-                         int32_t *out_i, double *margin)
+                         const gate_opts *opt, double *s, double *v,
+                         double *mv, int *keep, double *gs, int *chosen,
+                         int64_t *sel, double *out_w, int32_t *out_i,
+                         double *margin)
 {
     const int64_t S = E / G;
 
-    /* Step 2: s = 1 / (1 + exp(-L)). */
-    for (int64_t e = 0; e < E; ++e) s[e] = 1.0 / (1.0 + exp(-L[e]));
+    /* Step 2: affinities. */
+    if (opt->score_func == 0) {
+        /* s = 1 / (1 + exp(-L)) */
+        for (int64_t e = 0; e < E; ++e) s[e] = 1.0 / (1.0 + exp(-L[e]));
+    } else {
+        /* s = exp(L) / sum exp(L), shifted by the maximum for range */
+        double mx = -INFINITY, sum = 0.0;
+        for (int64_t e = 0; e < E; ++e) mx = L[e] > mx ? L[e] : mx;
+        for (int64_t e = 0; e < E; ++e) sum += exp(L[e] - mx);
+        for (int64_t e = 0; e < E; ++e) s[e] = exp(L[e] - mx) / sum;
+    }
 
     /* Step 3: the bias shifts the choice score only. */
-    for (int64_t e = 0; e < E; ++e) v[e] = s[e] + (double)bias[e];
+    for (int64_t e = 0; e < E; ++e) v[e] = s[e] + (bias ? (double)bias[e] : 0.0);
 
     /* Steps 4-5: group scores and group keep mask. */
     for (int g = 0; g < G; ++g) keep[g] = 1;
@@ -148,7 +181,10 @@ static void select_token(const double *L, const float *bias, int64_t E, int G,
                     top2 = v[e];
                 }
             }
-            gs[g] = top1 + top2;
+            if (bias)
+                gs[g] = top1 + top2;
+            else
+                gs[g] = top1;   /* no bias: the group maximum */
         }
         /* a group is kept when fewer than KG groups precede it */
         for (int g = 0; g < G; ++g) {
@@ -171,29 +207,33 @@ static void select_token(const double *L, const float *bias, int64_t E, int G,
         }
     }
 
-    /* Step 5 (mask) and step 6: repeatedly take the best remaining
-     * candidate; experts of dropped groups count as -inf and are never
-     * taken because K <= KG*S. */
+    /* Step 5: experts of dropped groups take the fill value. */
+    const double fill = opt->mask_zero ? 0.0 : -INFINITY;
+    for (int64_t e = 0; e < E; ++e) mv[e] = keep[e / S] ? v[e] : fill;
+
+    /* Step 6: repeatedly take the best remaining expert of the masked
+     * scores.  With the -inf fill, dropped experts are never taken because
+     * K <= KG*S. */
     for (int64_t e = 0; e < E; ++e) chosen[e] = 0;
     for (int k = 0; k < K; ++k) {
         int64_t best = -1;
         for (int64_t e = 0; e < E; ++e) {
-            if (!keep[e / S] || chosen[e]) continue;
-            if (best < 0 || precedes(v[e], e, v[best], best)) best = e;
+            if (chosen[e]) continue;
+            if (best < 0 || precedes(mv[e], e, mv[best], best)) best = e;
         }
         chosen[best] = 1;
         sel[k] = best;
     }
-    /* margin between the K-th winner and the best loser among candidates */
+    /* margin between the K-th winner and the best loser */
     {
         double best_loser = -INFINITY;
         int any = 0;
         for (int64_t e = 0; e < E; ++e) {
-            if (!keep[e / S] || chosen[e]) continue;
-            if (!any || v[e] > best_loser) best_loser = v[e];
+            if (chosen[e] || mv[e] == -INFINITY) continue;
+            if (!any || mv[e] > best_loser) best_loser = mv[e];
             any = 1;
         }
-        margin[0] = any ? v[sel[K - 1]] - best_loser : INFINITY;
+        margin[0] = any ? mv[sel[K - 1]] - best_loser : INFINITY;
     }
 
     /* canonical order: ascending expert id */
@@ -210,83 +250,105 @@ static void select_token(const double *L, const float *bias, int64_t E, int G,
     }
 
     /* Steps 7-8: gather unbiased s, renormalise, scale. */
+    const int renorm = opt->renorm == 0 ? opt->score_func == 0 : opt->renorm == 1;
     double denom = 0.0;
     for (int k = 0; k < K; ++k) denom += s[sel[k]];
+    denom += opt->denom_eps;
     for (int k = 0; k < K; ++k) {
         out_i[k] = (int32_t)sel[k];
-        out_w[k] = s[sel[k]] / denom * route_scale;
+        if (renorm)
+            out_w[k] = s[sel[k]] / denom * route_scale;
+        else
+            out_w[k] = s[sel[k]] * route_scale;
     }
 }
 
-/* Gate from precomputed float64 logits [T, E].
+static int check_opts(int score_func, int renorm, int mask_zero)
+{
+    if (score_func != 0 && score_func != 1) return ORACLE_EINVAL;
+    if (renorm < 0 || renorm > 2) return ORACLE_EINVAL;
+    if (mask_zero != 0 && mask_zero != 1) return ORACLE_EINVAL;
+    return ORACLE_OK;
+}
+
+/* Gate from precomputed float64 logits [T, E]; bias may be NULL.
  *   margins may be NULL; otherwise [T, 2]. */
 int oracle_select(const double *logits, const float *bias, int64_t T,
                   int64_t E, int G, int KG, int K, double route_scale,
-                  int order, double *weights, int32_t *indices,
+                  int order, int score_func, int renorm, int mask_zero,
+                  double denom_eps, double *weights, int32_t *indices,
                   double *margins)
 {
     if (check_cfg(E, G, KG, K) != ORACLE_OK) return ORACLE_EINVAL;
     if (order != 0 && order != 1) return ORACLE_EINVAL;
+    if (check_opts(score_func, renorm, mask_zero) != ORACLE_OK) return ORACLE_EINVAL;
+    const gate_opts opt = {score_func, renorm, mask_zero, denom_eps};
     int failed = 0;
 #pragma omp parallel
     {
         double *s = malloc(sizeof(double) * E);
         double *v = malloc(sizeof(double) * E);
+        double *mv = malloc(sizeof(double) * E);
         double *gs = malloc(sizeof(double) * G);
         int *keep = malloc(sizeof(int) * G);
         int *chosen = malloc(sizeof(int) * E);
         int64_t *sel = malloc(sizeof(int64_t) * K);
         double mdummy[2];
-        if (!s || !v || !gs || !keep || !chosen || !sel) {
+        if (!s || !v || !mv || !gs || !keep || !chosen || !sel) {
 #pragma omp atomic write
             failed = 1;
         } else {
 #pragma omp for schedule(static)
             for (int64_t t = 0; t < T; ++t)
                 select_token(logits + t * E, bias, E, G, KG, K, route_scale,
-                             order, s, v, keep, gs, chosen, sel,
+                             order, &opt, s, v, mv, keep, gs, chosen, sel,
                              weights + t * K, indices + t * K,
                              margins ? margins + 2 * t : mdummy);
         }
-        free(s); free(v); free(gs); free(keep); free(chosen); free(sel);
+        free(s); free(v); free(mv); free(gs); free(keep); free(chosen); free(sel);
     }
     return failed ? ORACLE_EINVAL : ORACLE_OK;
 }
 
 /* Whole gate from x (bfloat16 bits, [T, d]), W (float32, [E, d]) and bias
- * (float32, [E]).  Logits are computed token by token and never stored. */
+ * (float32, [E], or NULL).  Logits are computed token by token and never
+ * stored. */
 int oracle_gate(const uint16_t *x, const float *W, const float *bias,
                 int64_t T, int64_t d, int64_t E, int G, int KG, int K,
-                double route_scale, int order, double *weights,
+                double route_scale, int order, int score_func, int renorm,
+                int mask_zero, double denom_eps, double *weights,
                 int32_t *indices, double *margins)
 {
     if (check_cfg(E, G, KG, K) != ORACLE_OK || d <= 0) return ORACLE_EINVAL;
     if (order != 0 && order != 1) return ORACLE_EINVAL;
+    if (check_opts(score_func, renorm, mask_zero) != ORACLE_OK) return ORACLE_EINVAL;
+    const gate_opts opt = {score_func, renorm, mask_zero, denom_eps};
     int failed = 0;
 #pragma omp parallel
     {
         double *L = malloc(sizeof(double) * E);
         double *s = malloc(sizeof(double) * E);
         double *v = malloc(sizeof(double) * E);
+        double *mv = malloc(sizeof(double) * E);
         double *gs = malloc(sizeof(double) * G);
         int *keep = malloc(sizeof(int) * G);
         int *chosen = malloc(sizeof(int) * E);
         int64_t *sel = malloc(sizeof(int64_t) * K);
         double mdummy[2];
-        if (!L || !s || !v || !gs || !keep || !chosen || !sel) {
+        if (!L || !s || !v || !mv || !gs || !keep || !chosen || !sel) {
 #pragma omp atomic write
             failed = 1;
         } else {
 #pragma omp for schedule(static)
             for (int64_t t = 0; t < T; ++t) {
                 logits_row(x + t * d, W, d, E, L);
-                select_token(L, bias, E, G, KG, K, route_scale, order, s, v,
-                             keep, gs, chosen, sel, weights + t * K,
+                select_token(L, bias, E, G, KG, K, route_scale, order, &opt,
+                             s, v, mv, keep, gs, chosen, sel, weights + t * K,
                              indices + t * K,
                              margins ? margins + 2 * t : mdummy);
             }
         }
-        free(L); free(s); free(v); free(gs); free(keep); free(chosen);
+        free(L); free(s); free(v); free(mv); free(gs); free(keep); free(chosen);
         free(sel);
     }
     return failed ? ORACLE_EINVAL : ORACLE_OK;
@@ -332,6 +394,39 @@ int oracle_gather_rows(const uint16_t *x, int64_t T, int64_t d, int K,
         int64_t p = perm[pos];
         if (p < 0 || p / K >= T) return ORACLE_EINVAL;
         memcpy(out + pos * d, x + (p / K) * d, sizeof(uint16_t) * (size_t)d);
+    }
+    return ORACLE_OK;
+}
+
+/* Combine: y[t, :] = sum_k w[t, k] * out[dest[t*K + k], :], where out is
+ * the expert output in dispatch (expert-major) order, bfloat16 bits
+ * [n_pos, d], and dest[p] is the position of pair p = t*K + k.  The sum is
+ * float64 in ascending k; y64 receives it, and y16 (if not NULL) receives
+ * it rounded to float32 and then to bfloat16 (round to nearest even), the
+ * two roundings of a float32 sum cast back to the activation type. */
+int oracle_combine(const uint16_t *out, int64_t n_pos, const double *w,
+                   const int32_t *dest, int64_t T, int K, int64_t d,
+                   double *y64, uint16_t *y16)
+{
+    for (int64_t p = 0; p < T * (int64_t)K; ++p)
+        if (dest[p] < 0 || dest[p] >= n_pos) return ORACLE_EINVAL;
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+        for (int64_t j = 0; j < d; ++j) {
+            double acc = 0.0;
+            for (int k = 0; k < K; ++k) {
+                const int64_t pos = dest[t * K + k];
+                acc += w[t * K + k] * bf16_to_double(out[pos * d + j]);
+            }
+            y64[t * d + j] = acc;
+            if (y16) {
+                float f = (float)acc;
+                uint32_t u;
+                memcpy(&u, &f, sizeof u);
+                u += 0x7fffu + ((u >> 16) & 1u);   /* round to nearest even */
+                y16[t * d + j] = (uint16_t)(u >> 16);
+            }
+        }
     }
     return ORACLE_OK;
 }

@@ -38,15 +38,19 @@ def _is_top_set(members, values, pool):
     return all(_precedes(values[m], m, values[r], r) for m in members for r in rest)
 
 
-def brute_force_gate(v, E, G, KG, K):
+def brute_force_gate(v, E, G, KG, K, group_max=False, fill=None):
     """Selected expert set by exhaustive enumeration.  Group score is the
-    best pair sum inside the group (= sum of its two largest members);
-    exactly one group subset and one expert subset may satisfy the top-set
-    property."""
+    best pair sum inside the group (= sum of its two largest members), or the
+    best single member when ``group_max``; exactly one group subset and one
+    expert subset may satisfy the top-set property.  Experts of dropped
+    groups are excluded, or -- with ``fill`` -- compete with value ``fill``."""
     S = E // G
     if G > 1:
-        gs = [max(v[g * S + i] + v[g * S + j]
-                  for i in range(S) for j in range(i + 1, S)) for g in range(G)]
+        if group_max:
+            gs = [max(v[g * S + i] for i in range(S)) for g in range(G)]
+        else:
+            gs = [max(v[g * S + i] + v[g * S + j]
+                      for i in range(S) for j in range(i + 1, S)) for g in range(G)]
         kept = [c for c in itertools.combinations(range(G), KG)
                 if _is_top_set(set(c), gs, range(G))]
         assert len(kept) == 1, "group top-set not unique"
@@ -54,8 +58,13 @@ def brute_force_gate(v, E, G, KG, K):
     else:
         gs = None
         kept = (0,)
-    cand = [e for e in range(E) if e // S in kept]
-    sets = [c for c in itertools.combinations(cand, K) if _is_top_set(set(c), v, cand)]
+    if fill is None:
+        cand = [e for e in range(E) if e // S in kept]
+        vals = v
+    else:
+        cand = list(range(E))
+        vals = [v[e] if e // S in kept else fill for e in range(E)]
+    sets = [c for c in itertools.combinations(cand, K) if _is_top_set(set(c), vals, cand)]
     assert len(sets) == 1, "expert top-set not unique"
     return sorted(sets[0]), kept, gs, cand
 
@@ -299,8 +308,117 @@ def pin_dispatch(o):
             assert np.array_equal(rows, x[r.perm // K])
 
 
+def pin_softmax_scores(o):
+    """Softmax scoring: the affinities are scipy's softmax over all E
+    logits; the selection is the enumerated top set of softmax + bias; with
+    the default rule the K weights are NOT renormalised (route_scale times
+    the gathered probabilities), and forcing renormalisation makes them sum
+    to route_scale."""
+    from scipy.special import softmax
+    rng = np.random.default_rng(23)
+    for (E, G, KG, K) in [(16, 4, 2, 4), (12, 3, 2, 3), (16, 1, 1, 5)]:
+        for _ in range(4):
+            L, b = _discrete_case(rng, E)
+            sm = softmax(L)
+            want, _, _, _ = brute_force_gate(sm + b.astype(np.float64), E, G, KG, K)
+            r = o.select(L[None, :], b, G, KG, K, 1.5, score_func=1)
+            assert list(r.indices[0]) == want
+            assert np.allclose(r.weights[0], 1.5 * sm[want], rtol=1e-12, atol=0)
+            r1 = o.select(L[None, :], b, G, KG, K, 1.5, score_func=1, renorm=1)
+            assert np.allclose(r1.weights[0].sum(), 1.5, rtol=1e-12)
+            assert np.allclose(r1.weights[0], 1.5 * sm[want] / sm[want].sum(), rtol=1e-12)
+
+
+def pin_no_bias_group_max(o):
+    """No bias: the choice score is the affinity and a group scores by its
+    largest member (enumerated); sigmoid weights still renormalise."""
+    rng = np.random.default_rng(24)
+    for (E, G, KG, K) in [(8, 4, 2, 3), (16, 4, 2, 4), (16, 8, 3, 5), (24, 6, 2, 4)]:
+        for trial in range(4):
+            L, _ = _discrete_case(rng, E, tie=(trial % 2 == 1))
+            s = expit(L)
+            want, _, _, _ = brute_force_gate(s, E, G, KG, K, group_max=True)
+            r = o.select(L[None, :], None, G, KG, K, 2.0)
+            assert list(r.indices[0]) == want
+            assert np.allclose(r.weights[0], 2.0 * s[want] / s[want].sum(), rtol=1e-12)
+
+
+def pin_renorm_off(o):
+    """renorm=2 (off) with sigmoid: each weight is route_scale * sigmoid of
+    its logit (scipy expit)."""
+    rng = np.random.default_rng(25)
+    L = rng.standard_normal((20, 64))
+    b = rng.uniform(-0.05, 0.05, size=64).astype(np.float32)
+    r = o.select(L, b, 8, 4, 8, 2.5, renorm=2)
+    s = expit(np.take_along_axis(L, r.indices.astype(np.int64), axis=1))
+    assert np.allclose(r.weights, 2.5 * s, rtol=1e-12, atol=0)
+
+
+def pin_mask_zero(o):
+    """mask_zero: experts of dropped groups compete with value 0.0 (the
+    Kimi K2 page's masked_fill), so with negative choice scores in the kept
+    groups the zero-filled experts win, lowest ids first (enumeration)."""
+    rng = np.random.default_rng(26)
+    for (E, G, KG, K) in [(16, 4, 2, 4), (12, 3, 2, 5), (16, 8, 3, 6)]:
+        for shift in (0.0, -0.9):
+            L, b = _discrete_case(rng, E)
+            b = (b + np.float32(shift)).astype(np.float32)
+            v = expit(L) + b.astype(np.float64)
+            want, kept, _, _ = brute_force_gate(v, E, G, KG, K, fill=0.0)
+            r = o.select(L[None, :], b, G, KG, K, 1.0, mask_zero=1)
+            assert list(r.indices[0]) == want
+            if shift < 0:
+                S = E // G
+                assert any(e // S not in kept for e in want), "case does not exercise the fill"
+
+
+def pin_denominator_epsilon(o):
+    """An epsilon in the denominator is invisible at ordinary scores but
+    dominates when every affinity underflows towards zero: logits near -700
+    give s ~ 1e-304, so with epsilon 1e-20 the weights collapse to ~0 while
+    without it they still sum to route_scale."""
+    L = np.full((1, 16), -700.0) + np.arange(16)[None, :] * 0.01
+    b = np.zeros(16, np.float32)
+    r0 = o.select(L, b, 1, 1, 4, 2.827)
+    r1 = o.select(L, b, 1, 1, 4, 2.827, denom_eps=1e-20)
+    assert np.isclose(r0.weights.sum(), 2.827, rtol=1e-12)
+    assert r1.weights.max() < 1e-250
+    Ln = np.random.default_rng(27).standard_normal((5, 16))
+    a = o.select(Ln, b, 1, 1, 4, 2.827)
+    c = o.select(Ln, b, 1, 1, 4, 2.827, denom_eps=1e-20)
+    assert np.array_equal(a.indices, c.indices)
+    assert np.allclose(a.weights, c.weights, rtol=1e-15, atol=0)
+
+
+def pin_combine(o):
+    """Combine: equals numpy's float64 einsum over the un-permuted rows; with
+    identity experts (outputs = dispatched rows) it returns
+    (sum of the token's weights) * x, i.e. route_scale * x for gate weights."""
+    from sigmoid_group_limited_amd.workloads import bf16_bits, bf16_to_f32, random_indices
+    rng = np.random.default_rng(28)
+    T, K, E, d = 37, 8, 32, 24
+    idx = random_indices(T, K, E, seed=5)
+    disp = o.dispatch(idx, E)
+    dest = np.empty(T * K, np.int32)
+    dest[disp.perm] = np.arange(T * K, dtype=np.int32)
+    outs = bf16_bits(rng.standard_normal((T * K, d), dtype=np.float32))
+    w = rng.uniform(0, 1, size=(T, K))
+    y64, y16 = o.combine(outs, w, dest)
+    rows = bf16_to_f32(outs).astype(np.float64)[dest.reshape(T, K)]
+    want = np.einsum("tk,tkd->td", w, rows)
+    assert np.allclose(y64, want, rtol=0, atol=1e-12)
+    assert np.array_equal(y16, bf16_bits(y64.astype(np.float32)))
+    x = bf16_bits(rng.standard_normal((T, d), dtype=np.float32))
+    gw = o.select(rng.standard_normal((T, E)), np.zeros(E, np.float32), 1, 1, K, 2.827).weights
+    ident = o.gather_rows(x, disp.perm, K)
+    y64, _ = o.combine(ident, gw, dest)
+    assert np.allclose(y64, 2.827 * bf16_to_f32(x).astype(np.float64), rtol=1e-12, atol=1e-300)
+
+
 ALL_PINS = [pin_exact_integer_logits, pin_logits_vs_matmul, pin_brute_force_selection,
             pin_zero_input_closed_form, pin_bias_shift_invariance,
             pin_weights_follow_unbiased_sigmoid, pin_winners_in_kept_groups,
             pin_single_group_no_bias_is_topk_of_logits, pin_permutation_equivariance,
-            pin_margins, pin_selection_order, pin_dispatch]
+            pin_margins, pin_selection_order, pin_dispatch, pin_softmax_scores,
+            pin_no_bias_group_max, pin_renorm_off, pin_mask_zero, pin_denominator_epsilon,
+            pin_combine]
