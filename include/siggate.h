@@ -42,7 +42,8 @@
  *   E in {128, 256, 384}; n_group a power of two with 1 <= n_group <= 64;
  *   1 <= top_k <= 8; d a positive multiple of 8; 0 <= T <= 2^31 / top_k.
  * Invalid configurations return SIGGATE_EINVAL: topk_group outside
- * [1, n_group], top_k > topk_group * E / n_group, order not 0 or 1.
+ * [1, n_group], top_k > topk_group * E / n_group, order not 0 or 1,
+ * score_func, renorm or mask_zero out of range, denom_eps negative or NaN.
  */
 #ifndef SIGGATE_H
 #define SIGGATE_H
@@ -66,6 +67,15 @@ typedef struct siggate_cfg {
     int32_t order;       /* output order of a token's top_k entries:
                             0 = ascending expert id,
                             1 = choice score descending (index ascending on ties) */
+    /* Variants of the gate (all zero = the DeepSeek-V3 / Kimi-K2 gate above).
+     * Sources: DeepSeek-V3.2-Exp · Normalize weights, "Code" (softmax branch;
+     * group maximum without a bias; renormalise only for sigmoid) and Kimi K2
+     * · Normalize weights, "Code" (0.0 fill of dropped groups, 1e-20 added to
+     * the denominator, renormalisation behind a config flag). */
+    int32_t score_func;  /* 0 = sigmoid, 1 = softmax over the E logits        */
+    int32_t renorm;      /* 0 = renormalise iff sigmoid, 1 = always, 2 = never */
+    int32_t mask_zero;   /* 0 = dropped groups -> -inf, 1 = -> 0.0             */
+    float denom_eps;     /* added to the renormalisation denominator (>= 0)   */
 } siggate_cfg_t;
 
 typedef enum siggate_status {
@@ -84,7 +94,10 @@ size_t siggate_workspace_bytes(const siggate_cfg_t *cfg);
 /* Gate.
  *   x        bfloat16 [T, d]  (raw bfloat16 bits)
  *   W        float32  [E, d]  (router weight, one row per expert)
- *   bias     float32  [E]     (selection-only bias; required)
+ *   bias     float32  [E]     (selection-only bias), or NULL: then the choice
+ *                             score is the affinity itself and a group scores
+ *                             by its largest member (DeepSeek-V3.2-Exp · Normalize
+ *                             weights, "Code": the branch without a bias)
  *   weights  float32  [T, top_k]  out: route_scale * renormalised s
  *   indices  int32    [T, top_k]  out: selected expert ids
  *   ws       device workspace of ws_bytes >= siggate_workspace_bytes(cfg)
@@ -115,6 +128,22 @@ siggate_status_t siggate_dispatch(const void *x, const int32_t *indices,
                                   int32_t *tokens_per_expert, int32_t *offsets,
                                   int32_t *perm, int32_t *dest, void *permuted_x,
                                   void *ws, size_t ws_bytes, void *stream);
+
+/* Combine (Kimi K2 · Add shared output, "Code": moe_infer, last lines):
+ * un-permute the expert outputs and add each token's top_k rows weighted by
+ * its gate weights, in float32, then round to bfloat16 (nearest even):
+ *   y[t, :] = bf16( sum_k weights[t, k] * expert_out[dest[t*top_k + k], :] )
+ * with the sum taken in ascending k.
+ *   expert_out  bfloat16 [n_pos, d] in dispatch (expert-major) order,
+ *               n_pos = T * top_k
+ *   weights     float32 [T, top_k]  (siggate_forward's weights)
+ *   dest        int32 [T*top_k]     (siggate_dispatch's dest); entries
+ *               outside [0, n_pos) are skipped (contribute nothing)
+ *   y           bfloat16 [T, d]     out
+ * Only T, d and top_k of cfg are used; needs no workspace. */
+siggate_status_t siggate_combine(const void *expert_out, const float *weights,
+                                 const int32_t *dest, const siggate_cfg_t *cfg,
+                                 void *y, void *stream);
 
 /* Test hook: the float32 logits L = x . W^T [T, E] that siggate_forward
  * selects from, computed by the same kernels in the same summation order

@@ -6,10 +6,10 @@ binding (``binding``), the in-tree build (``build``) and the seeded synthetic
 inputs (``workloads``).  Importing the package does not load the library;
 the first call does, and raises if it is not built.
 """
-from .binding import (Cfg, DispatchOut, SiggateError, load_library, siggate_dispatch,
-                      siggate_forward, siggate_logits, siggate_status_str,
+from .binding import (Cfg, DispatchOut, SiggateError, load_library, siggate_combine,
+                      siggate_dispatch, siggate_forward, siggate_logits, siggate_status_str,
                       siggate_workspace_bytes, workspace)
 
-__all__ = ["Cfg", "DispatchOut", "SiggateError", "load_library", "siggate_dispatch",
-           "siggate_forward", "siggate_logits", "siggate_status_str",
+__all__ = ["Cfg", "DispatchOut", "SiggateError", "load_library", "siggate_combine",
+           "siggate_dispatch", "siggate_forward", "siggate_logits", "siggate_status_str",
            "siggate_workspace_bytes", "workspace"]

@@ -8,6 +8,7 @@ cannot be loaded the call raises -- there is no fallback path.
 from __future__ import annotations
 
 import ctypes
+import dataclasses
 import os
 from dataclasses import dataclass
 
@@ -22,7 +23,7 @@ SIGGATE_EHIP = -4
 
 # Symbols declared in include/siggate.h
 EXPORTS = ("siggate_workspace_bytes", "siggate_forward", "siggate_dispatch",
-           "siggate_logits", "siggate_status_str")
+           "siggate_combine", "siggate_logits", "siggate_status_str")
 
 
 class SiggateError(RuntimeError):
@@ -35,12 +36,14 @@ class siggate_cfg_t(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int32), ("d", ctypes.c_int32), ("E", ctypes.c_int32),
                 ("n_group", ctypes.c_int32), ("topk_group", ctypes.c_int32),
                 ("top_k", ctypes.c_int32), ("route_scale", ctypes.c_float),
-                ("order", ctypes.c_int32)]
+                ("order", ctypes.c_int32), ("score_func", ctypes.c_int32),
+                ("renorm", ctypes.c_int32), ("mask_zero", ctypes.c_int32),
+                ("denom_eps", ctypes.c_float)]
 
 
 @dataclass(frozen=True)
 class Cfg:
-    """Python mirror of siggate_cfg_t."""
+    """Python mirror of siggate_cfg_t (see include/siggate.h)."""
     T: int
     d: int
     E: int
@@ -49,14 +52,18 @@ class Cfg:
     top_k: int
     route_scale: float
     order: int = 0
+    score_func: int = 0      # 0 sigmoid, 1 softmax
+    renorm: int = 0          # 0 iff sigmoid, 1 always, 2 never
+    mask_zero: int = 0       # dropped groups: 0 -> -inf, 1 -> 0.0
+    denom_eps: float = 0.0   # added to the renormalisation denominator
 
     def c(self) -> siggate_cfg_t:
         return siggate_cfg_t(self.T, self.d, self.E, self.n_group, self.topk_group,
-                             self.top_k, self.route_scale, self.order)
+                             self.top_k, self.route_scale, self.order, self.score_func,
+                             self.renorm, self.mask_zero, self.denom_eps)
 
     def with_T(self, T: int) -> "Cfg":
-        return Cfg(T, self.d, self.E, self.n_group, self.topk_group, self.top_k,
-                   self.route_scale, self.order)
+        return dataclasses.replace(self, T=T)
 
 
 _lib = None
@@ -79,6 +86,8 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
     lib.siggate_forward.argtypes = [vp, vp, vp, cfgp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.siggate_dispatch.restype = ctypes.c_int
     lib.siggate_dispatch.argtypes = [vp, vp, cfgp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.siggate_combine.restype = ctypes.c_int
+    lib.siggate_combine.argtypes = [vp, vp, vp, cfgp, vp, vp]
     lib.siggate_logits.restype = ctypes.c_int
     lib.siggate_logits.argtypes = [vp, vp, cfgp, vp, vp, ctypes.c_size_t, vp]
     lib.siggate_status_str.restype = ctypes.c_char_p
@@ -134,7 +143,7 @@ def workspace(cfg: Cfg, device=None):
 def siggate_forward(x, W, bias, cfg: Cfg, weights=None, indices=None, ws=None, stream=None):
     """Gate: returns (weights float32 [T, top_k], indices int32 [T, top_k]).
     x is bfloat16 (or int16 bit patterns) [T, d]; W float32 [E, d]; bias
-    float32 [E]."""
+    float32 [E] or None (the no-bias variant)."""
     import torch
     T, K = cfg.T, cfg.top_k
     dev = x.device
@@ -146,7 +155,8 @@ def siggate_forward(x, W, bias, cfg: Cfg, weights=None, indices=None, ws=None, s
         ws = workspace(cfg, dev)
     _check_dev("x", x, 2, cfg.T * cfg.d)
     _check_dev("W", W, 4, cfg.E * cfg.d)
-    _check_dev("bias", bias, 4, cfg.E)
+    if bias is not None:
+        _check_dev("bias", bias, 4, cfg.E)
     _check_dev("weights", weights, 4, T * K)
     _check_dev("indices", indices, 4, T * K)
     c = cfg.c()
@@ -218,3 +228,22 @@ def siggate_dispatch(x, indices, cfg: Cfg, out: DispatchOut | None = None, ws=No
     if rc != SIGGATE_OK:
         raise SiggateError(rc, "siggate_dispatch")
     return out
+
+
+def siggate_combine(expert_out, weights, dest, cfg: Cfg, y=None, stream=None):
+    """y[t] = bf16(sum_k weights[t,k] * expert_out[dest[t*K+k]]) : bfloat16
+    [T, d] from expert outputs in dispatch order [T*K, d]."""
+    import torch
+    T, K, d = cfg.T, cfg.top_k, cfg.d
+    if y is None:
+        y = torch.empty((T, d), dtype=expert_out.dtype, device=expert_out.device)
+    _check_dev("expert_out", expert_out, 2, T * K * d)
+    _check_dev("weights", weights, 4, T * K)
+    _check_dev("dest", dest, 4, T * K)
+    _check_dev("y", y, 2, T * d)
+    c = cfg.c()
+    rc = load_library().siggate_combine(_ptr(expert_out), _ptr(weights), _ptr(dest),
+                                        ctypes.byref(c), _ptr(y), _stream(stream))
+    if rc != SIGGATE_OK:
+        raise SiggateError(rc, "siggate_combine")
+    return y

@@ -25,6 +25,10 @@ siggate_status_t check_gate_cfg(const siggate_cfg_t *c)
     if ((long long)c->top_k > (long long)c->topk_group * (c->E / c->n_group)) return SIGGATE_EINVAL;
     if (c->order != 0 && c->order != 1) return SIGGATE_EINVAL;
     if (!(c->route_scale == c->route_scale)) return SIGGATE_EINVAL;   // NaN
+    if (c->score_func != 0 && c->score_func != 1) return SIGGATE_EINVAL;
+    if (c->renorm < 0 || c->renorm > 2) return SIGGATE_EINVAL;
+    if (c->mask_zero != 0 && c->mask_zero != 1) return SIGGATE_EINVAL;
+    if (!(c->denom_eps >= 0.0f)) return SIGGATE_EINVAL;               // negative or NaN
     if (c->E != 128 && c->E != 256 && c->E != 384) return SIGGATE_EUNSUPPORTED;
     if (c->n_group > 64 || (c->n_group & (c->n_group - 1)) != 0) return SIGGATE_EUNSUPPORTED;
     if (c->top_k > MAX_TOPK) return SIGGATE_EUNSUPPORTED;
@@ -63,6 +67,10 @@ GateArgs gate_args(const void *x, const float *W, const float *bias, const sigga
     a.top_k = c->top_k;
     a.order = c->order;
     a.route_scale = c->route_scale;
+    a.score_func = c->score_func;
+    a.renorm = c->renorm;
+    a.mask_zero = c->mask_zero;
+    a.denom_eps = c->denom_eps;
     a.chunks_total = (c->d + KC - 1) / KC;
     a.chunks_per_split = p.chunks_per_split;
     a.n_split = p.n_split;
@@ -90,7 +98,7 @@ siggate_status_t siggate_forward(const void *x, const float *W, const float *bia
 {
     siggate_status_t st = check_gate_cfg(cfg);
     if (st != SIGGATE_OK) return st;
-    if (!W || !bias) return SIGGATE_EINVAL;
+    if (!W) return SIGGATE_EINVAL;   // bias may be NULL (no-bias variant)
     if (cfg->T > 0 && (!x || !weights || !indices)) return SIGGATE_EINVAL;
     if (!aligned16(x) || !aligned16(W) || !aligned16(bias) || !aligned16(weights) ||
         !aligned16(indices) || !aligned16(ws))
@@ -163,6 +171,29 @@ siggate_status_t siggate_dispatch(const void *x, const int32_t *indices, const s
     a.perm = perm;
     a.permuted_x = (uint16_t *)permuted_x;
     return launch_dispatch(a, (hipStream_t)stream) == hipSuccess ? SIGGATE_OK : SIGGATE_EHIP;
+}
+
+siggate_status_t siggate_combine(const void *expert_out, const float *weights,
+                                 const int32_t *dest, const siggate_cfg_t *cfg, void *y,
+                                 void *stream)
+{
+    if (!cfg) return SIGGATE_EINVAL;
+    if (cfg->T < 0 || cfg->d <= 0 || cfg->top_k <= 0) return SIGGATE_EINVAL;
+    if (cfg->top_k > MAX_TOPK || cfg->d % 8 != 0) return SIGGATE_EUNSUPPORTED;
+    if ((long long)cfg->T * cfg->top_k > 0x7fffffffLL) return SIGGATE_EUNSUPPORTED;
+    if (cfg->T > 0 && (!expert_out || !weights || !dest || !y)) return SIGGATE_EINVAL;
+    if (!aligned16(expert_out) || !aligned16(weights) || !aligned16(dest) || !aligned16(y))
+        return SIGGATE_EINVAL;
+    if (cfg->T == 0) return SIGGATE_OK;
+    CombineArgs a;
+    a.expert_out = (const uint16_t *)expert_out;
+    a.weights = weights;
+    a.dest = dest;
+    a.y = (uint16_t *)y;
+    a.T = cfg->T;
+    a.d = cfg->d;
+    a.top_k = cfg->top_k;
+    return launch_combine(a, (hipStream_t)stream) == hipSuccess ? SIGGATE_OK : SIGGATE_EHIP;
 }
 
 const char *siggate_status_str(siggate_status_t status)

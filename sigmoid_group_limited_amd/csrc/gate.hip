@@ -93,11 +93,31 @@ __device__ __forceinline__ void select_token(const float (&lg)[V], const float (
                                              float *scratch)
 {
     float s[V], v[V];
+    if (a.score_func == 0) {
 #pragma unroll
-    for (int j = 0; j < V; ++j) {
-        s[j] = 1.0f / (1.0f + expf(-lg[j]));
-        v[j] = s[j] + bias_r[j];
+        for (int j = 0; j < V; ++j) s[j] = 1.0f / (1.0f + expf(-lg[j]));
+    } else {
+        // softmax over the E logits of the token (wave-wide max and sum; the
+        // butterfly gives every lane the same bits)
+        float mx = lg[0];
+#pragma unroll
+        for (int j = 1; j < V; ++j) mx = fmaxf(mx, lg[j]);
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+        float sum = 0.0f;
+#pragma unroll
+        for (int j = 0; j < V; ++j) {
+            s[j] = expf(lg[j] - mx);
+            sum += s[j];
+        }
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off);
+#pragma unroll
+        for (int j = 0; j < V; ++j) s[j] = s[j] / sum;
     }
+    // without a bias, bias_r is 0 and v equals s
+#pragma unroll
+    for (int j = 0; j < V; ++j) v[j] = s[j] + bias_r[j];
 
     const int G = a.n_group;
     if (G > 1) {
@@ -123,7 +143,8 @@ __device__ __forceinline__ void select_token(const float (&lg)[V], const float (
             m2 = fmaxf(lo, fmaxf(m2, o2));
             m1 = hi;
         }
-        const float gs = m1 + m2;
+        // with a bias: top-2 sum; without: the group maximum
+        const float gs = a.bias ? m1 + m2 : m1;
         const int g = lane / lpg;
         // Rank of this lane's group under (score desc, group index asc).
         int ahead = 0;
@@ -132,8 +153,9 @@ __device__ __forceinline__ void select_token(const float (&lg)[V], const float (
             ahead += (gh > gs) || (gh == gs && h < g);
         }
         if (ahead >= a.topk_group) {
+            const float fill = a.mask_zero ? 0.0f : -INFINITY;
 #pragma unroll
-            for (int j = 0; j < V; ++j) v[j] = -INFINITY;
+            for (int j = 0; j < V; ++j) v[j] = fill;
         }
     }
 
@@ -189,8 +211,10 @@ __device__ __forceinline__ void select_token(const float (&lg)[V], const float (
 
     // Renormalise over the K winners (unbiased s, summed in ascending id
     // order) and scale; lane k < K writes one entry.
+    const bool renorm = a.renorm == 0 ? a.score_func == 0 : a.renorm == 1;
     float denom = 0.0f;
     for (int k = 0; k < K; ++k) denom += scratch[k];
+    denom += a.denom_eps;
     if (lane < K) {
         const float my_s = scratch[lane];
         const int my_i = __float_as_int(scratch[MAX_TOPK + lane]);
@@ -204,7 +228,8 @@ __device__ __forceinline__ void select_token(const float (&lg)[V], const float (
             }
         }
         a.indices[(size_t)t * K + pos] = my_i;
-        a.weights[(size_t)t * K + pos] = my_s / denom * a.route_scale;
+        a.weights[(size_t)t * K + pos] = renorm ? my_s / denom * a.route_scale
+                                                : my_s * a.route_scale;
     }
     __builtin_amdgcn_wave_barrier();
 }
@@ -256,7 +281,7 @@ __device__ __forceinline__ void finish_tile(const GateArgs &a,
         constexpr int V = S::V;
         float bias_r[V];
 #pragma unroll
-        for (int j = 0; j < V; ++j) bias_r[j] = a.bias[lane * V + j];
+        for (int j = 0; j < V; ++j) bias_r[j] = a.bias ? a.bias[lane * V + j] : 0.0f;
 
         for (int i = 0; i < S::BM / NW; ++i) {
             const int row = wave * (S::BM / NW) + i;
@@ -505,7 +530,7 @@ __global__ __launch_bounds__(RED_NT) void gate_reduce_kernel(GateArgs a)
     } else {
         float bias_r[V];
 #pragma unroll
-        for (int j = 0; j < V; ++j) bias_r[j] = a.bias[lane * V + j];
+        for (int j = 0; j < V; ++j) bias_r[j] = a.bias ? a.bias[lane * V + j] : 0.0f;
         select_token<V>(lg, bias_r, lane, a, t, scratch);
     }
 }

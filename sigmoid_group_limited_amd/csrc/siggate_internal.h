@@ -25,7 +25,8 @@ struct GateArgs {
     const float *bias;      // [E]
     int T, d;
     int n_group, topk_group, top_k, order;
-    float route_scale;
+    int score_func, renorm, mask_zero;
+    float route_scale, denom_eps;
     int chunks_total;       // ceil(d / KC)
     int chunks_per_split;   // KC-chunks handled by one blockIdx.y
     int n_split;            // gridDim.y of the GEMM launch
@@ -65,5 +66,14 @@ struct DispatchArgs {
 
 size_t dispatch_workspace_bytes(int T, int E, int top_k, bool need_dest);
 hipError_t launch_dispatch(const DispatchArgs &a, hipStream_t stream);
+
+struct CombineArgs {
+    const uint16_t *expert_out;   // bfloat16 [T * top_k, d]
+    const float *weights;         // [T, top_k]
+    const int32_t *dest;          // [T * top_k]
+    uint16_t *y;                  // bfloat16 [T, d]
+    int T, d, top_k;
+};
+hipError_t launch_combine(const CombineArgs &a, hipStream_t stream);
 
 }  // namespace siggate

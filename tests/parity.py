@@ -35,7 +35,7 @@ def dev_inputs(gi, device="cuda"):
 
 
 def compare_gate(w_gpu: np.ndarray, i_gpu: np.ndarray, ref, route_scale: float,
-                 rows: np.ndarray | None = None):
+                 rows: np.ndarray | None = None, check_sum: bool = True):
     """Compare GPU weights/indices (full [T, K] arrays, or ``rows`` of them)
     with an oracle result on the same rows.  Returns a stats dict; raises
     AssertionError on a non-exempt index mismatch or a weight outside
@@ -59,8 +59,9 @@ def compare_gate(w_gpu: np.ndarray, i_gpu: np.ndarray, ref, route_scale: float,
     assert stats["weight_max_rel"] <= WEIGHT_RTOL, stats
     # properties that hold for every token, exempt or not
     assert np.all(w_gpu >= 0)
-    sums = w_gpu.astype(np.float64).sum(1)
-    assert np.allclose(sums, route_scale, rtol=1e-5, atol=0), "weights do not sum to route_scale"
+    if check_sum:
+        sums = w_gpu.astype(np.float64).sum(1)
+        assert np.allclose(sums, route_scale, rtol=1e-5, atol=0), "weights do not sum to route_scale"
     return stats
 
 

@@ -73,6 +73,8 @@ def call_dispatch(cfg, x=FAKE, idx=FAKE, tpe=FAKE, off=FAKE, perm=FAKE, dest=FAK
     dict(n_group=3), dict(topk_group=0), dict(topk_group=9), dict(top_k=0),
     dict(top_k=33, topk_group=1), dict(order=2), dict(T=-1), dict(d=0),
     dict(route_scale=float("nan")), dict(E=256, n_group=256, topk_group=1, top_k=1),
+    dict(score_func=2), dict(renorm=3), dict(renorm=-1), dict(mask_zero=2),
+    dict(denom_eps=-1e-20), dict(denom_eps=float("nan")),
 ])
 def test_forward_rejects_invalid(bad):
     fields = DSV3.__dict__ | bad
@@ -91,7 +93,7 @@ def test_forward_rejects_unsupported(unsup):
 
 def test_forward_pointer_and_workspace_checks():
     assert call_forward(DSV3, x=0) == binding.SIGGATE_EINVAL
-    assert call_forward(DSV3, bias=0) == binding.SIGGATE_EINVAL
+    assert call_forward(DSV3, W=0) == binding.SIGGATE_EINVAL
     assert call_forward(DSV3, W=FAKE + 4) == binding.SIGGATE_EINVAL
     assert call_forward(DSV3, w=FAKE + 8) == binding.SIGGATE_EINVAL
     need = sg.siggate_workspace_bytes(DSV3)
@@ -128,3 +130,32 @@ def test_python_binding_rejects_host_tensors():
         sg.siggate_forward(x, W, b, DSV3, weights=torch.zeros((64, 8)),
                            indices=torch.zeros((64, 8), dtype=torch.int32),
                            ws=torch.zeros(1 << 20, dtype=torch.uint8))
+
+
+def call_combine(cfg, out=FAKE, w=FAKE, dest=FAKE, y=FAKE):
+    c = cfg.c()
+    return sg.load_library().siggate_combine(out, w, dest, ctypes.byref(c), y, None)
+
+
+def test_combine_checks():
+    cfg = DSV3.with_T(100)
+    assert call_combine(cfg.__class__(**(cfg.__dict__ | dict(top_k=9)))) == \
+        binding.SIGGATE_EUNSUPPORTED
+    assert call_combine(cfg.__class__(**(cfg.__dict__ | dict(d=12)))) == \
+        binding.SIGGATE_EUNSUPPORTED
+    assert call_combine(cfg.__class__(**(cfg.__dict__ | dict(top_k=0)))) == binding.SIGGATE_EINVAL
+    assert call_combine(cfg, out=0) == binding.SIGGATE_EINVAL
+    assert call_combine(cfg, dest=FAKE + 4) == binding.SIGGATE_EINVAL
+    assert call_combine(cfg.with_T(0), out=0, w=0, dest=0, y=0) == binding.SIGGATE_OK
+
+
+def test_cfg_struct_layout():
+    """The ctypes mirror matches the C struct: 12 four-byte fields."""
+    assert ctypes.sizeof(binding.siggate_cfg_t) == 48
+    names = [f[0] for f in binding.siggate_cfg_t._fields_]
+    with open(HEADER) as f:
+        text = f.read()
+    body = text[text.index("typedef struct siggate_cfg {"):text.index("} siggate_cfg_t;")]
+    body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
+    declared = re.findall(r"(?:int32_t|float)\s+(\w+);", body)
+    assert declared == names
