@@ -101,6 +101,16 @@ class Oracle:
         lib.oracle_gather_rows.argtypes = [P(ctypes.c_uint16), i64, i64, i32,
                                            P(ctypes.c_int32), i64,
                                            P(ctypes.c_uint16)]
+        lib.oracle_ep_send_splits.restype = i32
+        lib.oracle_ep_send_splits.argtypes = [P(ctypes.c_int32), i64, i32,
+                                              P(ctypes.c_int32), P(ctypes.c_int32)]
+        lib.oracle_ep_regroup.restype = i32
+        lib.oracle_ep_regroup.argtypes = [P(ctypes.c_int32), i32, i64,
+                                          P(ctypes.c_int32), P(ctypes.c_int32)]
+        lib.oracle_ep_dedup.restype = i32
+        lib.oracle_ep_dedup.argtypes = [P(ctypes.c_int32), i64, i32, i64, i32,
+                                        P(ctypes.c_int32), P(ctypes.c_int32),
+                                        P(ctypes.c_int32), P(ctypes.c_int32)]
         lib.oracle_combine.restype = i32
         lib.oracle_combine.argtypes = [P(ctypes.c_uint16), i64, P(dbl),
                                        P(ctypes.c_int32), i64, i32, i64,
@@ -237,6 +247,50 @@ class Oracle:
         if rc != OK:
             raise ValueError("oracle_combine: dest entry out of range")
         return y64, y16
+
+
+    # -- expert-parallel metadata --------------------------------------
+    def ep_send_splits(self, tokens_per_expert: np.ndarray, ep_size: int):
+        """(send_counts [ep_size], send_offsets [ep_size+1]): per-rank sums
+        of tokens_per_expert."""
+        tpe = np.ascontiguousarray(tokens_per_expert, dtype=np.int32)
+        c = np.empty(ep_size, np.int32)
+        off = np.empty(ep_size + 1, np.int32)
+        rc = self.lib.oracle_ep_send_splits(_ptr(tpe, ctypes.c_int32), tpe.shape[0], ep_size,
+                                            _ptr(c, ctypes.c_int32), _ptr(off, ctypes.c_int32))
+        if rc != OK:
+            raise ValueError("oracle_ep_send_splits: E not a multiple of ep_size")
+        return c, off
+
+    def ep_regroup(self, counts: np.ndarray):
+        """counts [ep_size, experts_per_rank] of received rows ->
+        (local_counts [experts_per_rank], regroup [n_recv])."""
+        cnt = np.ascontiguousarray(counts, dtype=np.int32)
+        R, per = cnt.shape
+        n = int(cnt.sum())
+        lc = np.empty(per, np.int32)
+        rg = np.empty(max(n, 1), np.int32)
+        rc = self.lib.oracle_ep_regroup(_ptr(cnt, ctypes.c_int32), R, per,
+                                        _ptr(lc, ctypes.c_int32), _ptr(rg, ctypes.c_int32))
+        if rc != OK:
+            raise ValueError("oracle_ep_regroup rejected its input")
+        return lc, rg[:n]
+
+    def ep_dedup(self, indices: np.ndarray, n_experts: int, ep_size: int):
+        """De-duplicated rank-major send list: (rank_counts, rank_offsets,
+        send_tokens, pair_slot)."""
+        idx = np.ascontiguousarray(indices, dtype=np.int32)
+        T, K = idx.shape
+        rcnt = np.empty(ep_size, np.int32)
+        roff = np.empty(ep_size + 1, np.int32)
+        send = np.empty(max(T * K, 1), np.int32)
+        slot = np.empty(max(T * K, 1), np.int32)
+        rc = self.lib.oracle_ep_dedup(_ptr(idx, ctypes.c_int32), T, K, n_experts, ep_size,
+                                      _ptr(rcnt, ctypes.c_int32), _ptr(roff, ctypes.c_int32),
+                                      _ptr(send, ctypes.c_int32), _ptr(slot, ctypes.c_int32))
+        if rc != OK:
+            raise ValueError("oracle_ep_dedup rejected its input")
+        return rcnt, roff, send[:int(roff[-1])], slot[:T * K]
 
 
 _DEFAULT: Oracle | None = None

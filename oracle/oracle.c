@@ -430,3 +430,108 @@ int oracle_combine(const uint16_t *out, int64_t n_pos, const double *w,
     }
     return ORACLE_OK;
 }
+
+/* ---------------------------------------------------------------------
+ * Expert-parallel metadata on one GPU (Kimi K2 · Add shared output,
+ * "Code": moe_infer, the ep_size > 1 branch).  Experts are split into
+ * ep_size ranks of experts_per_rank = E / ep_size consecutive experts.
+ * ------------------------------------------------------------------- */
+
+/* Rows each rank receives from this one: the per-rank sums of
+ * tokens_per_expert (the pages' tokens_per_ep_rank / input_split_sizes),
+ * and their exclusive prefix. */
+int oracle_ep_send_splits(const int32_t *tokens_per_expert, int64_t E, int ep_size,
+                          int32_t *send_counts, int32_t *send_offsets)
+{
+    if (ep_size <= 0 || E % ep_size != 0) return ORACLE_EINVAL;
+    const int64_t per = E / ep_size;
+    send_offsets[0] = 0;
+    for (int r = 0; r < ep_size; ++r) {
+        int32_t c = 0;
+        for (int64_t j = 0; j < per; ++j) c += tokens_per_expert[r * per + j];
+        send_counts[r] = c;
+        send_offsets[r + 1] = send_offsets[r] + c;
+    }
+    return ORACLE_OK;
+}
+
+/* Receive-side regroup.  counts[r * per + j] rows arrive from source rank r
+ * for local expert j, rank after rank and, within a rank, in local-expert
+ * order.  Each received row is labelled with its local expert id; the rows
+ * are then put in label order (the pages' argsort of gatherd_idxs), stably,
+ * so rows of one expert keep their arrival order.
+ *   local_counts[j] = sum_r counts[r, j]   (tokens_per_expert_post_gather)
+ *   regroup[q] = index of the received row that goes to position q. */
+int oracle_ep_regroup(const int32_t *counts, int ep_size, int64_t per,
+                      int32_t *local_counts, int32_t *regroup)
+{
+    if (ep_size <= 0 || per <= 0) return ORACLE_EINVAL;
+    int64_t n = 0;
+    for (int64_t i = 0; i < ep_size * per; ++i) {
+        if (counts[i] < 0) return ORACLE_EINVAL;
+        n += counts[i];
+    }
+    int32_t *label = malloc(sizeof(int32_t) * (size_t)(n ? n : 1));
+    if (!label) return ORACLE_EINVAL;
+    int64_t s = 0;
+    for (int r = 0; r < ep_size; ++r)
+        for (int64_t j = 0; j < per; ++j)
+            for (int32_t c = 0; c < counts[r * per + j]; ++c) label[s++] = (int32_t)j;
+    /* stable counting sort of the labels */
+    for (int64_t j = 0; j < per; ++j) local_counts[j] = 0;
+    for (int64_t i = 0; i < n; ++i) local_counts[label[i]] += 1;
+    int32_t *fill = malloc(sizeof(int32_t) * (size_t)per);
+    if (!fill) { free(label); return ORACLE_EINVAL; }
+    int32_t run = 0;
+    for (int64_t j = 0; j < per; ++j) { fill[j] = run; run += local_counts[j]; }
+    for (int64_t i = 0; i < n; ++i) regroup[fill[label[i]]++] = (int32_t)i;
+    free(fill);
+    free(label);
+    return ORACLE_OK;
+}
+
+/* De-duplicated send list: a token whose top-K experts sit on one rank
+ * several times is sent to that rank once.  For rank r = e / per:
+ *   rank_counts[r]       distinct tokens sent to rank r
+ *   rank_offsets[r]      exclusive prefix of rank_counts
+ *   send_tokens[pos]     token ids, rank-major, ascending token inside a rank
+ *   pair_slot[t*K + k]   position in send_tokens of (t, rank of its k-th expert)
+ * Walks the tokens in ascending order and, per token, its K slots in order. */
+int oracle_ep_dedup(const int32_t *indices, int64_t T, int K, int64_t E, int ep_size,
+                    int32_t *rank_counts, int32_t *rank_offsets, int32_t *send_tokens,
+                    int32_t *pair_slot)
+{
+    if (ep_size <= 0 || E % ep_size != 0 || K <= 0) return ORACLE_EINVAL;
+    const int64_t per = E / ep_size;
+    for (int64_t p = 0; p < T * K; ++p)
+        if (indices[p] < 0 || indices[p] >= E) return ORACLE_EINVAL;
+    for (int r = 0; r < ep_size; ++r) rank_counts[r] = 0;
+    for (int64_t t = 0; t < T; ++t)
+        for (int r = 0; r < ep_size; ++r) {
+            int hit = 0;
+            for (int k = 0; k < K; ++k) hit |= indices[t * K + k] / per == r;
+            rank_counts[r] += hit;
+        }
+    rank_offsets[0] = 0;
+    for (int r = 0; r < ep_size; ++r) rank_offsets[r + 1] = rank_offsets[r] + rank_counts[r];
+    int32_t *fill = malloc(sizeof(int32_t) * (size_t)ep_size);
+    if (!fill) return ORACLE_EINVAL;
+    for (int r = 0; r < ep_size; ++r) fill[r] = rank_offsets[r];
+    for (int64_t t = 0; t < T; ++t) {
+        for (int k = 0; k < K; ++k) {
+            const int r = (int)(indices[t * K + k] / per);
+            int first = k;   /* first slot of this token on rank r */
+            for (int k2 = 0; k2 < k; ++k2)
+                if (indices[t * K + k2] / per == r) { first = k2; break; }
+            if (first == k) {
+                send_tokens[fill[r]] = (int32_t)t;
+                pair_slot[t * K + k] = fill[r];
+                fill[r] += 1;
+            } else {
+                pair_slot[t * K + k] = pair_slot[t * K + first];
+            }
+        }
+    }
+    free(fill);
+    return ORACLE_OK;
+}

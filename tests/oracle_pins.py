@@ -415,10 +415,87 @@ def pin_combine(o):
     assert np.allclose(y64, 2.827 * bf16_to_f32(x).astype(np.float64), rtol=1e-12, atol=1e-300)
 
 
+def _ep_case(rng, T, K, E):
+    from sigmoid_group_limited_amd.workloads import random_indices
+    return random_indices(T, K, E, seed=int(rng.integers(1 << 30)))
+
+
+def pin_ep_send_splits(o):
+    """Per-rank send splits are numpy's segment sums of tokens_per_expert."""
+    rng = np.random.default_rng(29)
+    for (E, R) in [(256, 8), (384, 8), (384, 3), (16, 16), (16, 1)]:
+        tpe = rng.integers(0, 1000, size=E).astype(np.int32)
+        c, off = o.ep_send_splits(tpe, R)
+        assert np.array_equal(c, tpe.reshape(R, -1).sum(1))
+        assert np.array_equal(off, np.r_[0, np.cumsum(c)])
+
+
+def pin_ep_regroup(o):
+    """Receive-side regroup is a stable library argsort of the received
+    rows' local-expert labels; and end to end, simulating the exchange with
+    numpy between R ranks that each dispatch their own tokens, every rank
+    ends up with, per local expert, the rows all sources sent for it, source
+    rank by source rank in the sources' dispatch order."""
+    rng = np.random.default_rng(30)
+    for (R, per) in [(8, 32), (4, 3), (1, 5), (3, 1)]:
+        counts = rng.integers(0, 6, size=(R, per)).astype(np.int32)
+        lc, rg = o.ep_regroup(counts)
+        labels = np.repeat(np.tile(np.arange(per), R), counts.ravel())
+        assert np.array_equal(rg, np.argsort(labels, kind="stable"))
+        assert np.array_equal(lc, counts.sum(0))
+    R, T, K, E, d = 4, 50, 4, 32, 3
+    per = E // R
+    xs = [rng.integers(0, 65536, size=(T, d), dtype=np.uint16) for _ in range(R)]
+    idxs = [_ep_case(rng, T, K, E) for _ in range(R)]
+    sent = []            # sent[src][dst] = rows in src's dispatch order
+    sent_counts = []     # sent_counts[src][dst, j]
+    for src in range(R):
+        disp = o.dispatch(idxs[src], E)
+        rows = o.gather_rows(xs[src], disp.perm, K)
+        c, off = o.ep_send_splits(disp.counts, R)
+        sent.append([rows[off[r]:off[r + 1]] for r in range(R)])
+        sent_counts.append(disp.counts.reshape(R, per))
+    for dst in range(R):
+        received = np.concatenate([sent[src][dst] for src in range(R)])
+        counts = np.stack([sent_counts[src][dst] for src in range(R)])
+        lc, rg = o.ep_regroup(counts)
+        grouped = received[rg]
+        pos = 0
+        for j in range(per):
+            want = []
+            for src in range(R):
+                flat = idxs[src].ravel()
+                ps = np.nonzero(flat == dst * per + j)[0]      # ascending pair ids
+                want.append(xs[src][ps // K])
+            want = np.concatenate(want)
+            assert lc[j] == len(want)
+            assert np.array_equal(grouped[pos:pos + len(want)], want)
+            pos += len(want)
+
+
+def pin_ep_dedup(o):
+    """De-duplicated send list: rank r receives exactly the tokens with at
+    least one top-K expert on r, once each, ascending (numpy unique); every
+    pair's slot holds its own token inside its rank's segment."""
+    rng = np.random.default_rng(31)
+    for (T, K, E, R) in [(60, 8, 64, 8), (33, 4, 16, 4), (10, 3, 12, 1), (40, 8, 384, 48)]:
+        idx = _ep_case(rng, T, K, E)
+        per = E // R
+        rcnt, roff, send, slot = o.ep_dedup(idx, E, R)
+        for r in range(R):
+            want = np.unique(np.nonzero((idx // per == r).any(axis=1))[0])
+            assert rcnt[r] == len(want)
+            assert np.array_equal(send[roff[r]:roff[r + 1]], want)
+        tok = np.repeat(np.arange(T), K)
+        assert np.array_equal(send[slot], tok)
+        rank_of_slot = np.searchsorted(roff, slot, side="right") - 1
+        assert np.array_equal(rank_of_slot, idx.ravel() // per)
+
+
 ALL_PINS = [pin_exact_integer_logits, pin_logits_vs_matmul, pin_brute_force_selection,
             pin_zero_input_closed_form, pin_bias_shift_invariance,
             pin_weights_follow_unbiased_sigmoid, pin_winners_in_kept_groups,
             pin_single_group_no_bias_is_topk_of_logits, pin_permutation_equivariance,
             pin_margins, pin_selection_order, pin_dispatch, pin_softmax_scores,
             pin_no_bias_group_max, pin_renorm_off, pin_mask_zero, pin_denominator_epsilon,
-            pin_combine]
+            pin_combine, pin_ep_send_splits, pin_ep_regroup, pin_ep_dedup]

@@ -62,6 +62,12 @@ MUTANTS = [
      "for (int64_t p = n - 1; p >= 0; --p) {\n        int32_t e = indices[p];"),
     ("offsets_not_cumulative", "offsets[e + 1] = offsets[e] + counts[e];",
      "offsets[e + 1] = counts[e];"),
+    ("ep_splits_skip_last_expert", "for (int64_t j = 0; j < per; ++j) c += tokens_per_expert[r * per + j];",
+     "for (int64_t j = 0; j + 1 < per; ++j) c += tokens_per_expert[r * per + j];"),
+    ("ep_regroup_unstable", "for (int64_t i = 0; i < n; ++i) regroup[fill[label[i]]++] = (int32_t)i;",
+     "for (int64_t i = n - 1; i >= 0; --i) regroup[fill[label[i]]++] = (int32_t)i;"),
+    ("ep_dedup_keeps_duplicates", "if (indices[t * K + k2] / per == r) { first = k2; break; }",
+     "if (0) { first = k2; break; }"),
     ("gather_wrong_row", "memcpy(out + pos * d, x + (p / K) * d,",
      "memcpy(out + pos * d, x + (p % T) * d,"),
 ]
