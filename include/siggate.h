@@ -145,6 +145,47 @@ siggate_status_t siggate_combine(const void *expert_out, const float *weights,
                                  const int32_t *dest, const siggate_cfg_t *cfg,
                                  void *y, void *stream);
 
+/* Expert-parallel metadata on one GPU (Kimi K2 · Add shared output, "Code":
+ * moe_infer, the ep_size > 1 branch).  Experts are split into ep_size ranks
+ * of per = E / ep_size consecutive experts (E % ep_size must be 0).
+ *
+ * Send splits: send_counts[r] = sum of tokens_per_expert over rank r's
+ * experts (rows of the dispatch buffer that go to rank r, which are
+ * contiguous because expert-major order is rank-major), send_offsets [ep_size
+ * + 1] their exclusive prefix.  1 <= ep_size <= E <= 4096. */
+siggate_status_t siggate_ep_send_splits(const int32_t *tokens_per_expert, int32_t E,
+                                        int32_t ep_size, int32_t *send_counts,
+                                        int32_t *send_offsets, void *stream);
+
+/* Receive-side regroup.  counts [ep_size, per] (int32): rows received from
+ * source rank r for local expert j, in arrival order rank by rank and, in a
+ * rank, local expert by local expert.  Writes local_counts[j] = sum_r
+ * counts[r, j] and regroup[q] = arrival index of the row that goes to
+ * position q when the rows are put in local-expert order, stably (rows of one
+ * expert keep arrival order).  Positions q >= capacity are not written: size
+ * regroup by the received row count.  ep_size * per <= 4096. */
+siggate_status_t siggate_ep_regroup(const int32_t *counts, int32_t ep_size, int32_t per,
+                                    int32_t capacity, int32_t *local_counts,
+                                    int32_t *regroup, void *stream);
+
+/* De-duplicated send list: each token is sent once to every rank that holds
+ * at least one of its top_k experts.
+ *   indices       int32 [T, top_k] (the gate's indices; cfg gives T, E, top_k)
+ *   rank_counts   int32 [ep_size]      out, distinct tokens per rank
+ *   rank_offsets  int32 [ep_size + 1]  out, exclusive prefix
+ *   send_tokens   int32 [T * top_k]    out, first rank_offsets[ep_size]
+ *                 entries: token ids, rank-major, ascending in a rank
+ *   pair_slot     int32 [T * top_k]    out, position in send_tokens of
+ *                 (t, rank of the k-th expert of t)
+ *   ws            siggate_ep_workspace_bytes(cfg, ep_size) bytes
+ * ep_size <= 384. */
+size_t siggate_ep_workspace_bytes(const siggate_cfg_t *cfg, int32_t ep_size);
+siggate_status_t siggate_ep_dedup(const int32_t *indices, const siggate_cfg_t *cfg,
+                                  int32_t ep_size, int32_t *rank_counts,
+                                  int32_t *rank_offsets, int32_t *send_tokens,
+                                  int32_t *pair_slot, void *ws, size_t ws_bytes,
+                                  void *stream);
+
 /* Test hook: the float32 logits L = x . W^T [T, E] that siggate_forward
  * selects from, computed by the same kernels in the same summation order
  * (for the same T). */

@@ -23,7 +23,9 @@ SIGGATE_EHIP = -4
 
 # Symbols declared in include/siggate.h
 EXPORTS = ("siggate_workspace_bytes", "siggate_forward", "siggate_dispatch",
-           "siggate_combine", "siggate_logits", "siggate_status_str")
+           "siggate_combine", "siggate_ep_send_splits", "siggate_ep_regroup",
+           "siggate_ep_workspace_bytes", "siggate_ep_dedup", "siggate_logits",
+           "siggate_status_str")
 
 
 class SiggateError(RuntimeError):
@@ -88,6 +90,15 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
     lib.siggate_dispatch.argtypes = [vp, vp, cfgp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.siggate_combine.restype = ctypes.c_int
     lib.siggate_combine.argtypes = [vp, vp, vp, cfgp, vp, vp]
+    i32 = ctypes.c_int32
+    lib.siggate_ep_send_splits.restype = ctypes.c_int
+    lib.siggate_ep_send_splits.argtypes = [vp, i32, i32, vp, vp, vp]
+    lib.siggate_ep_regroup.restype = ctypes.c_int
+    lib.siggate_ep_regroup.argtypes = [vp, i32, i32, i32, vp, vp, vp]
+    lib.siggate_ep_workspace_bytes.restype = ctypes.c_size_t
+    lib.siggate_ep_workspace_bytes.argtypes = [cfgp, i32]
+    lib.siggate_ep_dedup.restype = ctypes.c_int
+    lib.siggate_ep_dedup.argtypes = [vp, cfgp, i32, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.siggate_logits.restype = ctypes.c_int
     lib.siggate_logits.argtypes = [vp, vp, cfgp, vp, vp, ctypes.c_size_t, vp]
     lib.siggate_status_str.restype = ctypes.c_char_p
@@ -247,3 +258,63 @@ def siggate_combine(expert_out, weights, dest, cfg: Cfg, y=None, stream=None):
     if rc != SIGGATE_OK:
         raise SiggateError(rc, "siggate_combine")
     return y
+
+
+# -- expert-parallel metadata ------------------------------------------------
+
+def siggate_ep_send_splits(tokens_per_expert, ep_size: int, stream=None):
+    """(send_counts [ep_size], send_offsets [ep_size + 1]) int32."""
+    import torch
+    E = tokens_per_expert.numel()
+    _check_dev("tokens_per_expert", tokens_per_expert, 4, E)
+    dev = tokens_per_expert.device
+    counts = torch.empty(ep_size, dtype=torch.int32, device=dev)
+    offsets = torch.empty(ep_size + 1, dtype=torch.int32, device=dev)
+    rc = load_library().siggate_ep_send_splits(_ptr(tokens_per_expert), E, ep_size,
+                                               _ptr(counts), _ptr(offsets), _stream(stream))
+    if rc != SIGGATE_OK:
+        raise SiggateError(rc, "siggate_ep_send_splits")
+    return counts, offsets
+
+
+def siggate_ep_regroup(counts, capacity: int, stream=None):
+    """counts [ep_size, per] int32 -> (local_counts [per], regroup [capacity])."""
+    import torch
+    R, per = counts.shape
+    _check_dev("counts", counts, 4, R * per)
+    dev = counts.device
+    local = torch.empty(per, dtype=torch.int32, device=dev)
+    regroup = torch.empty(max(capacity, 1), dtype=torch.int32, device=dev)
+    rc = load_library().siggate_ep_regroup(_ptr(counts), R, per, capacity, _ptr(local),
+                                           _ptr(regroup), _stream(stream))
+    if rc != SIGGATE_OK:
+        raise SiggateError(rc, "siggate_ep_regroup")
+    return local, regroup[:capacity]
+
+
+def siggate_ep_workspace_bytes(cfg: Cfg, ep_size: int) -> int:
+    c = cfg.c()
+    return int(load_library().siggate_ep_workspace_bytes(ctypes.byref(c), ep_size))
+
+
+def siggate_ep_dedup(indices, cfg: Cfg, ep_size: int, ws=None, stream=None):
+    """(rank_counts, rank_offsets, send_tokens [T*K], pair_slot [T*K]); the
+    first rank_offsets[-1] entries of send_tokens are valid."""
+    import torch
+    T, K = cfg.T, cfg.top_k
+    _check_dev("indices", indices, 4, T * K)
+    dev = indices.device
+    if ws is None:
+        ws = torch.empty(max(256, siggate_ep_workspace_bytes(cfg, ep_size)), dtype=torch.uint8,
+                         device=dev)
+    rcnt = torch.empty(ep_size, dtype=torch.int32, device=dev)
+    roff = torch.empty(ep_size + 1, dtype=torch.int32, device=dev)
+    send = torch.empty(max(T * K, 1), dtype=torch.int32, device=dev)
+    slot = torch.empty(max(T * K, 1), dtype=torch.int32, device=dev)
+    c = cfg.c()
+    rc = load_library().siggate_ep_dedup(_ptr(indices), ctypes.byref(c), ep_size, _ptr(rcnt),
+                                         _ptr(roff), _ptr(send), _ptr(slot), _ptr(ws),
+                                         ws.numel() * ws.element_size(), _stream(stream))
+    if rc != SIGGATE_OK:
+        raise SiggateError(rc, "siggate_ep_dedup")
+    return rcnt, roff, send, slot[:T * K]

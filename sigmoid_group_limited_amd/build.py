@@ -14,7 +14,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIBRARY = os.path.join(PKG, "libsiggate.so")
-SOURCES = ["gate.hip", "dispatch.hip", "combine.hip", "api.hip"]
+SOURCES = ["gate.hip", "dispatch.hip", "combine.hip", "ep.hip", "api.hip"]
 ARCH = "gfx950"
 
 # Packed fp32 arithmetic is switched off for all device code.

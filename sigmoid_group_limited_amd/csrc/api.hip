@@ -196,6 +196,103 @@ siggate_status_t siggate_combine(const void *expert_out, const float *weights,
     return launch_combine(a, (hipStream_t)stream) == hipSuccess ? SIGGATE_OK : SIGGATE_EHIP;
 }
 
+siggate_status_t siggate_ep_send_splits(const int32_t *tokens_per_expert, int32_t E,
+                                        int32_t ep_size, int32_t *send_counts,
+                                        int32_t *send_offsets, void *stream)
+{
+    if (E <= 0 || ep_size <= 0 || ep_size > E || E % ep_size != 0) return SIGGATE_EINVAL;
+    if (E > 4096) return SIGGATE_EUNSUPPORTED;
+    if (!tokens_per_expert || !send_counts || !send_offsets) return SIGGATE_EINVAL;
+    return launch_ep_send_splits(tokens_per_expert, E, ep_size, send_counts, send_offsets,
+                                 (hipStream_t)stream) == hipSuccess
+               ? SIGGATE_OK
+               : SIGGATE_EHIP;
+}
+
+siggate_status_t siggate_ep_regroup(const int32_t *counts, int32_t ep_size, int32_t per,
+                                    int32_t capacity, int32_t *local_counts,
+                                    int32_t *regroup, void *stream)
+{
+    if (ep_size <= 0 || per <= 0 || capacity < 0) return SIGGATE_EINVAL;
+    if ((long long)ep_size * per > 4096) return SIGGATE_EUNSUPPORTED;
+    if (!counts || !local_counts || (capacity > 0 && !regroup)) return SIGGATE_EINVAL;
+    return launch_ep_regroup(counts, ep_size, per, capacity, local_counts, regroup,
+                             (hipStream_t)stream) == hipSuccess
+               ? SIGGATE_OK
+               : SIGGATE_EHIP;
+}
+
+static siggate_status_t check_ep_dedup(const siggate_cfg_t *c, int32_t ep_size)
+{
+    if (!c || c->T < 0 || c->E <= 0 || c->top_k <= 0 || ep_size <= 0) return SIGGATE_EINVAL;
+    if (ep_size > c->E || c->E % ep_size != 0) return SIGGATE_EINVAL;
+    if (ep_size > MAX_EXPERTS || c->top_k > MAX_TOPK) return SIGGATE_EUNSUPPORTED;
+    if ((long long)c->T * c->top_k > 0x7fffffffLL) return SIGGATE_EUNSUPPORTED;
+    return SIGGATE_OK;
+}
+
+size_t siggate_ep_workspace_bytes(const siggate_cfg_t *cfg, int32_t ep_size)
+{
+    if (check_ep_dedup(cfg, ep_size) != SIGGATE_OK) return 0;
+    const size_t pairs = align256((size_t)cfg->T * cfg->top_k * sizeof(int32_t));
+    // rank ids, perm, dest, and the dispatch count tables over ranks
+    return 3 * pairs + dispatch_workspace_bytes(cfg->T, ep_size, cfg->top_k, false);
+}
+
+siggate_status_t siggate_ep_dedup(const int32_t *indices, const siggate_cfg_t *cfg,
+                                  int32_t ep_size, int32_t *rank_counts,
+                                  int32_t *rank_offsets, int32_t *send_tokens,
+                                  int32_t *pair_slot, void *ws, size_t ws_bytes,
+                                  void *stream)
+{
+    siggate_status_t st = check_ep_dedup(cfg, ep_size);
+    if (st != SIGGATE_OK) return st;
+    if (!rank_counts || !rank_offsets) return SIGGATE_EINVAL;
+    if (cfg->T > 0 && (!indices || !send_tokens || !pair_slot)) return SIGGATE_EINVAL;
+    if (!aligned16(indices) || !aligned16(rank_counts) || !aligned16(rank_offsets) ||
+        !aligned16(send_tokens) || !aligned16(pair_slot) || !aligned16(ws))
+        return SIGGATE_EINVAL;
+    const size_t need = siggate_ep_workspace_bytes(cfg, ep_size);
+    if (ws_bytes < need || (need && !ws)) return SIGGATE_EWORKSPACE;
+    const int T = cfg->T, K = cfg->top_k;
+    const size_t pairs = align256((size_t)T * K * sizeof(int32_t));
+    char *w = (char *)ws;
+    EpDedupArgs e;
+    memset(&e, 0, sizeof e);
+    e.indices = indices;
+    e.rank_ids = (int32_t *)w;
+    e.perm = (int32_t *)(w + pairs);
+    e.dest = (int32_t *)(w + 2 * pairs);
+    e.rank_offsets = rank_offsets;
+    e.send_tokens = send_tokens;
+    e.pair_slot = pair_slot;
+    e.T = T;
+    e.top_k = K;
+    e.per = cfg->E / ep_size;
+    e.ep_size = ep_size;
+
+    DispatchArgs a;
+    memset(&a, 0, sizeof a);
+    a.indices = e.rank_ids;
+    a.T = T;
+    a.d = 8;
+    a.E = ep_size;
+    a.top_k = K;
+    a.n_blocks = (T + DISPATCH_BLOCK_TOKENS - 1) / DISPATCH_BLOCK_TOKENS;
+    const size_t cnt_bytes = align256((size_t)a.n_blocks * ep_size * sizeof(int32_t));
+    a.block_counts = (int32_t *)(w + 3 * pairs);
+    a.block_base = (int32_t *)(w + 3 * pairs + cnt_bytes);
+    a.tokens_per_expert = rank_counts;
+    a.offsets = rank_offsets;
+    a.perm = e.perm;
+    a.dest = e.dest;
+
+    const hipStream_t s = (hipStream_t)stream;
+    if (launch_ep_dedup_map(e, s) != hipSuccess) return SIGGATE_EHIP;
+    if (launch_dispatch_meta(a, s) != hipSuccess) return SIGGATE_EHIP;
+    return launch_ep_dedup_finish(e, s) == hipSuccess ? SIGGATE_OK : SIGGATE_EHIP;
+}
+
 const char *siggate_status_str(siggate_status_t status)
 {
     switch (status) {

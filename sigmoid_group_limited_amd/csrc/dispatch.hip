@@ -214,6 +214,18 @@ size_t dispatch_workspace_bytes(int T, int E, int top_k, bool need_dest)
     return bytes;
 }
 
+hipError_t launch_dispatch_meta(const DispatchArgs &a, hipStream_t stream)
+{
+    if (a.n_blocks == 0) {
+        hipLaunchKernelGGL(dispatch_zero_kernel, dim3(1), dim3(BT), 0, stream, a);
+        return hipGetLastError();
+    }
+    hipLaunchKernelGGL(dispatch_count_kernel, dim3(a.n_blocks), dim3(BT), 0, stream, a);
+    hipLaunchKernelGGL(dispatch_scan_kernel, dim3(a.E), dim3(SCAN_THREADS), 0, stream, a);
+    hipLaunchKernelGGL(dispatch_scatter_kernel, dim3(a.n_blocks), dim3(BT), 0, stream, a);
+    return hipGetLastError();
+}
+
 hipError_t launch_dispatch(const DispatchArgs &a, hipStream_t stream)
 {
     if (a.n_blocks == 0) {

@@ -66,6 +66,25 @@ struct DispatchArgs {
 
 size_t dispatch_workspace_bytes(int T, int E, int top_k, bool need_dest);
 hipError_t launch_dispatch(const DispatchArgs &a, hipStream_t stream);
+// count, scan and scatter only (no row gather); dest must be set
+hipError_t launch_dispatch_meta(const DispatchArgs &a, hipStream_t stream);
+
+struct EpDedupArgs {
+    const int32_t *indices;   // [T, top_k]
+    int32_t *rank_ids;        // [T, top_k] workspace: rank of the slot, -1 if repeated
+    int32_t *perm;            // [T * top_k] workspace (scatter output)
+    int32_t *dest;            // [T * top_k] workspace (scatter output)
+    const int32_t *rank_offsets;   // [ep_size + 1] (scatter output)
+    int32_t *send_tokens;     // [<= T * top_k]
+    int32_t *pair_slot;       // [T * top_k]
+    int T, top_k, per, ep_size;
+};
+hipError_t launch_ep_send_splits(const int32_t *tpe, int E, int ep_size, int32_t *counts,
+                                 int32_t *offsets, hipStream_t stream);
+hipError_t launch_ep_regroup(const int32_t *counts, int ep_size, int per, int capacity,
+                             int32_t *local_counts, int32_t *regroup, hipStream_t stream);
+hipError_t launch_ep_dedup_map(const EpDedupArgs &a, hipStream_t stream);
+hipError_t launch_ep_dedup_finish(const EpDedupArgs &a, hipStream_t stream);
 
 struct CombineArgs {
     const uint16_t *expert_out;   // bfloat16 [T * top_k, d]

@@ -159,3 +159,23 @@ def test_cfg_struct_layout():
     body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
     declared = re.findall(r"(?:int32_t|float)\s+(\w+);", body)
     assert declared == names
+
+
+def test_ep_checks():
+    lib = sg.load_library()
+    c = DSV3.with_T(100).c()
+    assert lib.siggate_ep_send_splits(FAKE, 256, 3, FAKE, FAKE, None) == binding.SIGGATE_EINVAL
+    assert lib.siggate_ep_send_splits(FAKE, 256, 0, FAKE, FAKE, None) == binding.SIGGATE_EINVAL
+    assert lib.siggate_ep_send_splits(0, 256, 8, FAKE, FAKE, None) == binding.SIGGATE_EINVAL
+    assert lib.siggate_ep_regroup(FAKE, 8, 0, 10, FAKE, FAKE, None) == binding.SIGGATE_EINVAL
+    assert lib.siggate_ep_regroup(FAKE, 64, 128, 10, FAKE, FAKE, None) == \
+        binding.SIGGATE_EUNSUPPORTED
+    assert lib.siggate_ep_workspace_bytes(ctypes.byref(c), 3) == 0
+    need = lib.siggate_ep_workspace_bytes(ctypes.byref(c), 8)
+    assert need >= 3 * 100 * 8 * 4
+    assert lib.siggate_ep_dedup(FAKE, ctypes.byref(c), 3, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                1 << 30, None) == binding.SIGGATE_EINVAL
+    assert lib.siggate_ep_dedup(FAKE, ctypes.byref(c), 8, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                need - 256, None) == binding.SIGGATE_EWORKSPACE
+    assert lib.siggate_ep_dedup(FAKE, ctypes.byref(c), 8, FAKE, FAKE, FAKE + 4, FAKE, FAKE,
+                                need, None) == binding.SIGGATE_EINVAL
