@@ -125,6 +125,34 @@ class Case:
         disp_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
         return wall / steps * 1e3, gate_ms, disp_ms
 
+    def run_next_rows(self, steps: int, warmup: int):
+        """Times the steps after the path, on this workload's own outputs:
+        the combine (identity experts: the dispatched rows come back) and the
+        expert-parallel metadata for 8 ranks.  Returns a dict."""
+        import torch
+        sg = self.sg
+        y = torch.empty_like(self.x)
+        for _ in range(warmup):
+            sg.siggate_combine(self.out.permuted_x, self.weights, self.out.dest, self.cfg, y)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        torch.cuda.synchronize()
+        ev[0].record()
+        for _ in range(steps):
+            sg.siggate_combine(self.out.permuted_x, self.weights, self.out.dest, self.cfg, y)
+        ev[1].record()
+        for _ in range(steps):
+            sg.siggate_ep_send_splits(self.out.tokens_per_expert, 8)
+            sg.siggate_ep_dedup(self.indices, self.cfg, 8)
+        ev[2].record()
+        torch.cuda.synchronize()
+        T, K, d = self.w.T, self.cfg.top_k, self.w.d
+        comb_ms = ev[0].elapsed_time(ev[1]) / steps
+        comb_bytes = T * K * d * 2 + T * d * 2 + T * K * 8
+        return {"combine_ms": comb_ms,
+                "combine_algorithmic_GBps": comb_bytes / (comb_ms * 1e-3) / 1e9,
+                "combine_hbm_frac": comb_bytes / (comb_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                "ep8_metadata_ms": ev[1].elapsed_time(ev[2]) / steps}
+
     def algorithmic(self):
         T, d, E, K = self.w.T, self.w.d, self.cfg.E, self.cfg.top_k
         gate_flops = 2.0 * T * d * E
@@ -237,6 +265,7 @@ def main():
         },
     }
     result["stages"]["path_roofline_frac"] = result["value"] / result["stages"]["roofline_tokens_per_s"]
+    result["after_path"] = case.run_next_rows(max(3, args.steps // 2), 2)
     if args.secondary:
         sec = Case(args.secondary)
         ms2, g2, d2 = sec.run(args.steps, args.warmup)
