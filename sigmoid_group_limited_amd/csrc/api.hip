@@ -71,9 +71,13 @@ GateArgs gate_args(const void *x, const float *W, const float *bias, const sigga
     a.renorm = c->renorm;
     a.mask_zero = c->mask_zero;
     a.denom_eps = c->denom_eps;
+    a.E = c->E;
     a.chunks_total = (c->d + KC - 1) / KC;
     a.chunks_per_split = p.chunks_per_split;
     a.n_split = p.n_split;
+    a.t_tiles = p.t_tiles;
+    a.e_tiles = p.e_tiles;
+    a.n_tiles = p.t_tiles * p.e_tiles * p.n_split;
     return a;
 }
 

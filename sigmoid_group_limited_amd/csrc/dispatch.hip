@@ -8,7 +8,8 @@
 //          this is one of its valid results)
 //   permuted_x[pos] = x[perm[pos] / K]
 //
-// Four launches, none of them with order-dependent atomics:
+// Four launches (one for small batches, below), none of them with
+// order-dependent atomics:
 //   count   one block per 256 tokens; each wave ORs a 64-bit lane mask per
 //           expert in LDS (bit l = token l of the wave routes there), so the
 //           block's count of expert e is the popcount of its 4 masks;
@@ -193,6 +194,95 @@ __global__ __launch_bounds__(256) void dispatch_gather_kernel(DispatchArgs a)
     }
 }
 
+// Small batches (T * top_k <= SMALL_PAIRS): all of the dispatch in one
+// launch.  Block b handles token t = b / parts and the part-th slice of its
+// row.  Every block recounts all pairs from the (L2-resident) indices --
+// per-expert totals and the totals over tokens before t -- and takes the
+// exclusive prefix of the totals; pair (t, k) then lands at
+// offset[e] + before[e], since a token's experts are distinct and the
+// earlier pairs of expert e are exactly those of earlier tokens.  Counts
+// come from integer atomics, so the result does not depend on their order.
+constexpr int SMALL_PAIRS = 4096;
+constexpr int SMALL_NT = 256;
+
+__global__ __launch_bounds__(SMALL_NT) void dispatch_small_kernel(DispatchArgs a, int parts)
+{
+    __shared__ int cnt[MAX_EXPERTS];
+    __shared__ int before[MAX_EXPERTS];
+    __shared__ int offset[MAX_EXPERTS];
+    __shared__ int wave_tot[SMALL_NT / 64];
+    __shared__ int pos_s[MAX_TOPK];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int t = blockIdx.x / parts;
+    const int part = blockIdx.x - t * parts;
+    const int K = a.top_k;
+    const int first = t * K;              // pairs of tokens before t
+    const int npairs = a.T * K;
+    for (int x = tid; x < a.E; x += SMALL_NT) cnt[x] = before[x] = 0;
+    __syncthreads();
+    for (int p = tid; p < npairs; p += SMALL_NT) {
+        const int e = a.indices[p];
+        if ((unsigned)e < (unsigned)a.E) {
+            atomicAdd(&cnt[e], 1);
+            if (p < first) atomicAdd(&before[e], 1);
+        }
+    }
+    __syncthreads();
+    // exclusive prefix of cnt[] over experts, SMALL_NT experts at a time
+    int carry = 0;
+    for (int e0 = 0; e0 < a.E; e0 += SMALL_NT) {
+        const int x = e0 + tid;
+        const int c = x < a.E ? cnt[x] : 0;
+        int inc = c;
+        for (int off = 1; off < 64; off <<= 1) {
+            const int y = __shfl_up(inc, off);
+            if (lane >= off) inc += y;
+        }
+        if (lane == 63) wave_tot[wave] = inc;
+        __syncthreads();
+        int pre = carry, all = 0;
+        for (int w = 0; w < SMALL_NT / 64; ++w) {
+            pre += w < wave ? wave_tot[w] : 0;
+            all += wave_tot[w];
+        }
+        if (x < a.E) offset[x] = pre + inc - c;
+        carry += all;
+        __syncthreads();
+    }
+    if (blockIdx.x == 0) {
+        for (int x = tid; x < a.E; x += SMALL_NT) {
+            a.tokens_per_expert[x] = cnt[x];
+            if (a.offsets) a.offsets[x] = offset[x];
+        }
+        if (a.offsets && tid == 0) a.offsets[a.E] = carry;
+    }
+    if (tid < K) {
+        const int e = a.indices[first + tid];
+        const bool ok = (unsigned)e < (unsigned)a.E;
+        const int pos = ok ? offset[e] + before[e] : -1;
+        pos_s[tid] = pos;
+        if (part == 0) {
+            if (ok) a.perm[pos] = first + tid;
+            if (a.dest) a.dest[first + tid] = pos;
+        }
+    }
+    __syncthreads();
+    int dst[MAX_TOPK];
+#pragma unroll
+    for (int k = 0; k < MAX_TOPK; ++k) dst[k] = k < K ? pos_s[k] : -1;
+    const int nvec = a.d / 8;
+    const int per = (nvec + parts - 1) / parts;
+    const int v1 = min(nvec, (part + 1) * per);
+    const u32x4 *src = (const u32x4 *)(a.x + (size_t)t * a.d);
+    for (int i = part * per + tid; i < v1; i += SMALL_NT) {
+        const u32x4 val = src[i];
+#pragma unroll
+        for (int k = 0; k < MAX_TOPK; ++k)
+            if (dst[k] >= 0)
+                __builtin_nontemporal_store(val, (u32x4 *)(a.permuted_x + (size_t)dst[k] * a.d) + i);
+    }
+}
+
 // T == 0: every count and offset is zero.
 __global__ __launch_bounds__(BT) void dispatch_zero_kernel(DispatchArgs a)
 {
@@ -230,6 +320,14 @@ hipError_t launch_dispatch(const DispatchArgs &a, hipStream_t stream)
 {
     if (a.n_blocks == 0) {
         hipLaunchKernelGGL(dispatch_zero_kernel, dim3(1), dim3(BT), 0, stream, a);
+        return hipGetLastError();
+    }
+    if ((long)a.T * a.top_k <= SMALL_PAIRS) {
+        // split each row over enough blocks to reach about 256 of them
+        int parts = 1;
+        while ((long)a.T * parts * 2 <= 256 && parts * 2 <= a.d / 8) parts *= 2;
+        hipLaunchKernelGGL(dispatch_small_kernel, dim3(a.T * parts), dim3(SMALL_NT), 0, stream, a,
+                           parts);
         return hipGetLastError();
     }
     hipLaunchKernelGGL(dispatch_count_kernel, dim3(a.n_blocks), dim3(BT), 0, stream, a);

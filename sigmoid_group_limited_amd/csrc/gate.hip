@@ -11,16 +11,20 @@
 //   w = route_scale * s[winner] / sum(s[winners])
 //
 // Layout of the work
-//   One workgroup (4 waves) owns BM = 32*MB tokens and ALL E experts, so a
-//   token's whole score row ends in one workgroup and the selection never
-//   writes scores to HBM.  Wave w computes BM x (E/4) of the logits with
-//   v_mfma_f32_32x32x2_f32; operands come from LDS, which holds KC = 32
-//   k-columns of W [E x KC] and of x [BM x KC] (x upcast from bfloat16 to
-//   float32 on the way in, exact), double-buffered: the global loads of step
-//   c+1 are in flight while step c feeds the matrix cores.
-//   Small batches cut the k range into n_split slices (blockIdx.y); each
-//   slice writes float32 partial logits and a second kernel adds the slices
-//   in a fixed order (deterministic) and runs the same selection.
+//   One workgroup of 8 waves (two per SIMD) owns BM = 32*MB tokens and ALL E
+//   experts, so a token's whole score row ends in one workgroup and the
+//   selection never writes scores to HBM.  The waves are 4 expert quarters x
+//   2 token halves (BM = 64) or x 2 k-halves of every chunk (BM = 32); each
+//   computes its share of the logits with v_mfma_f32_32x32x2_f32.  Operands
+//   come from LDS, which holds KC = 32 k-columns of W [E x KC] and of x
+//   [BM x KC] (x upcast from bfloat16 to float32 on the way in, exact),
+//   double-buffered, with two more chunks of global loads in flight.
+//   Small batches (fewer than 256 such workgroups) use a split GEMM
+//   instead: a workgroup owns 32 or 64 tokens x 128 experts x one slice of
+//   the k range and writes float32 partial logits; a second kernel adds the
+//   slices in a fixed order (deterministic) and runs the same selection.
+//   Split tiles are ordered so that the token tiles sharing a W slice run on
+//   one XCD (one L2), and W crosses from HBM about once.
 #include <math.h>
 
 #include "siggate_internal.h"
@@ -32,7 +36,6 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int RED_NT = 256;     // threads per workgroup of the split-k reduction
 constexpr int KPAD = KC + 4;    // padded LDS row in floats: rows start 4 banks apart
 
 // Workgroup of NW waves: 4 expert quarters x WM token splits x KS k-splits.
@@ -239,19 +242,20 @@ __device__ __forceinline__ void select_token(const float (&lg)[V], const float (
 template <int E, int MB, int NW, int MODE>
 __device__ __forceinline__ void finish_tile(const GateArgs &a,
                                             f32x16 (&acc)[Shape<E, MB, NW>::MBW][Shape<E, MB, NW>::NB],
-                                            float *smem, const int t0, const int wave,
-                                            const int lane, const int wm, const bool has_acc)
+                                            float *smem, const int t0, const int e0, const int ks,
+                                            const int wave, const int lane, const int wm,
+                                            const bool has_acc)
 {
     using S = Shape<E, MB, NW>;
     const int wn = wave & 3;
     // Accumulator element r of block (m, n) in lane l is token
     // (wm*MBW + m)*32 + 8*(r/4) + 4*(l/32) + r%4 and expert
-    // wn*E/4 + n*32 + l%32.
-    const int e_base = wn * S::WCOLS + (lane & 31);
+    // e0 + wn*E/4 + n*32 + l%32 (E = experts of the tile).
+    const int e_base = e0 + wn * S::WCOLS + (lane & 31);
     const int r_base = wm * S::MBW * 32 + 4 * (lane >> 5);
 
     if constexpr (MODE == MODE_PARTIAL || MODE == MODE_LOGITS) {
-        float *out = MODE == MODE_PARTIAL ? a.partial + (size_t)blockIdx.y * a.T * E : a.logits;
+        float *out = MODE == MODE_PARTIAL ? a.partial + (size_t)ks * a.T * a.E : a.logits;
 #pragma unroll
         for (int m = 0; m < S::MBW; ++m)
 #pragma unroll
@@ -259,7 +263,7 @@ __device__ __forceinline__ void finish_tile(const GateArgs &a,
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int t = t0 + m * 32 + 8 * (r >> 2) + r_base + (r & 3);
-                    if (has_acc && t < a.T) out[(size_t)t * E + e_base + n * 32] = acc[m][n][r];
+                    if (has_acc && t < a.T) out[(size_t)t * a.E + e_base + n * 32] = acc[m][n][r];
                 }
     } else {
         // Scores go to LDS (never to HBM); each wave then selects for BM/NW
@@ -312,9 +316,23 @@ __global__ __launch_bounds__(64 * NW) void gate_gemm_kernel(GateArgs a)
     const int wn = wave & 3;                    // expert quarter of this wave
     const int wm = (wave >> 2) % S::WM;         // token split of this wave
     const int wk = (wave >> 2) / S::WM;         // k-split of this wave
-    const int t0 = blockIdx.x * S::BM;
+    int t0, e0 = 0, ks = 0;
+    if constexpr (MODE == MODE_PARTIAL) {
+        // Workgroup ids go round-robin over the 8 XCDs; each XCD gets one
+        // contiguous run of tile numbers (the grid is a multiple of 8).
+        // Tile numbers run token tile fastest, then expert tile, then
+        // k-slice, so the token tiles that read one W slice share an L2.
+        const int q = (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
+        if (q >= a.n_tiles) return;   // padding of the grid (whole workgroup)
+        const int r = q / a.t_tiles;
+        t0 = (q - r * a.t_tiles) * S::BM;
+        ks = r / a.e_tiles;
+        e0 = (r - ks * a.e_tiles) * E;
+    } else {
+        t0 = blockIdx.x * S::BM;
+    }
     const int d = a.d;
-    const int c_begin = blockIdx.y * a.chunks_per_split;
+    const int c_begin = ks * a.chunks_per_split;
     const int c_end = min(c_begin + a.chunks_per_split, a.chunks_total);
 
     // ---- global -> register staging.  Thread tid loads W rows
@@ -337,7 +355,7 @@ __global__ __launch_bounds__(64 * NW) void gate_gemm_kernel(GateArgs a)
     const int x_row = tid / XT;
     const int x_col = (tid % XT) * XE;
     const int x_t = min(t0 + x_row, a.T - 1);
-    const float *const Wp = a.W + (size_t)w_row * d;
+    const float *const Wp = a.W + (size_t)(e0 + w_row) * d;
     const uint16_t *const Xp = a.x + (size_t)x_t * d;
 
     auto load_global = [&](int c, Stage &st) {
@@ -381,6 +399,12 @@ __global__ __launch_bounds__(64 * NW) void gate_gemm_kernel(GateArgs a)
         for (int n = 0; n < S::NB; ++n)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[m][n][r] = 0.0f;
+    // A wave with a single 32x32 block alternates two accumulators (odd and
+    // even k-pairs), so consecutive MFMAs never wait on each other.
+    constexpr bool TWO_ACC = S::MBW * S::NB == 1;
+    f32x16 acc2;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc2[r] = 0.0f;
 
     const int f_row = lane & 31;
     const int f_k = (lane >> 5) * 4;
@@ -405,9 +429,14 @@ __global__ __launch_bounds__(64 * NW) void gate_gemm_kernel(GateArgs a)
 #pragma unroll
             for (int m = 0; m < S::MBW; ++m)
 #pragma unroll
-                for (int n = 0; n < S::NB; ++n)
-                    acc[m][n] = __builtin_amdgcn_mfma_f32_32x32x2f32(f.a[m][j], f.b[n][j],
-                                                                     acc[m][n], 0, 0, 0);
+                for (int n = 0; n < S::NB; ++n) {
+                    if (TWO_ACC && (j & 1))
+                        acc2 = __builtin_amdgcn_mfma_f32_32x32x2f32(f.a[m][j], f.b[n][j], acc2,
+                                                                    0, 0, 0);
+                    else
+                        acc[m][n] = __builtin_amdgcn_mfma_f32_32x32x2f32(f.a[m][j], f.b[n][j],
+                                                                         acc[m][n], 0, 0, 0);
+                }
     };
     static_assert(KC == 32, "the step below is written for four 8-column groups");
 
@@ -462,6 +491,11 @@ __global__ __launch_bounds__(64 * NW) void gate_gemm_kernel(GateArgs a)
         __syncthreads();   // every wave is done with the staging buffers
     }
 
+    if constexpr (TWO_ACC) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[0][0][r] += acc2[r];
+    }
+
     if constexpr (S::KS == 2) {
         // k-split pair: the second wave hands its sums to the first, which
         // adds them after its own (fixed order)
@@ -487,18 +521,42 @@ __global__ __launch_bounds__(64 * NW) void gate_gemm_kernel(GateArgs a)
         __syncthreads();
     }
 
-    finish_tile<E, MB, NW, MODE>(a, acc, smem, t0, wave, lane, wm, wk == 0);
+    finish_tile<E, MB, NW, MODE>(a, acc, smem, t0, e0, ks, wave, lane, wm, wk == 0);
+}
+
+// V consecutive floats from p (V even; p 8-byte aligned, 16-byte when V is
+// a multiple of 4).
+template <int V>
+__device__ __forceinline__ void load_row(const float *p, float (&v)[V])
+{
+    if constexpr (V % 4 == 0) {
+#pragma unroll
+        for (int h = 0; h < V / 4; ++h) {
+            const f32x4 q = *(const f32x4 *)(p + 4 * h);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[4 * h + i] = q[i];
+        }
+    } else {
+        static_assert(V % 2 == 0, "rows are loaded in float pairs");
+        typedef float f32x2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+        for (int h = 0; h < V / 2; ++h) {
+            const f32x2 q = *(const f32x2 *)(p + 2 * h);
+            v[2 * h] = q[0];
+            v[2 * h + 1] = q[1];
+        }
+    }
 }
 
 // Adds the n_split partial logits of one token in a fixed order -- wave w
-// sums its contiguous quarter of the slices, then wave 0 adds the four
-// quarter sums in wave order -- and writes the logits or runs the selection.
-// One workgroup per token.
-template <int E, int MODE>
-__global__ __launch_bounds__(RED_NT) void gate_reduce_kernel(GateArgs a)
+// of NWR sums its contiguous run of slices in ascending order, then wave 0
+// adds the runs in wave order -- and writes the logits or runs the
+// selection.  One workgroup per token; lane l owns experts [l*V, l*V + V).
+template <int E, int MODE, int NWR>
+__global__ __launch_bounds__(64 * NWR) void gate_reduce_kernel(GateArgs a)
 {
     constexpr int V = E / 64;
-    constexpr int NWR = RED_NT / 64;
+    constexpr int U = 4;   // slices loaded before they are added
     __shared__ float part[NWR][E];
     __shared__ float scratch[3 * MAX_TOPK];
     const int lane = threadIdx.x & 63;
@@ -507,14 +565,26 @@ __global__ __launch_bounds__(RED_NT) void gate_reduce_kernel(GateArgs a)
     const int per = (a.n_split + NWR - 1) / NWR;
     const int s0 = min(wave * per, a.n_split);
     const int s1 = min(s0 + per, a.n_split);
+    const float *const p = a.partial + (size_t)t * E + lane * V;
+    const size_t slice = (size_t)a.T * E;
     float lg[V];
 #pragma unroll
     for (int j = 0; j < V; ++j) lg[j] = 0.0f;
-#pragma unroll 4
-    for (int s = s0; s < s1; ++s) {
-        const float *p = a.partial + ((size_t)s * a.T + t) * E + lane * V;
+    int s = s0;
+    for (; s + U <= s1; s += U) {
+        float q[U][V];
 #pragma unroll
-        for (int j = 0; j < V; ++j) lg[j] += p[j];
+        for (int u = 0; u < U; ++u) load_row<V>(p + (size_t)(s + u) * slice, q[u]);
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int j = 0; j < V; ++j) lg[j] += q[u][j];
+    }
+    for (; s < s1; ++s) {
+        float q[V];
+        load_row<V>(p + (size_t)s * slice, q);
+#pragma unroll
+        for (int j = 0; j < V; ++j) lg[j] += q[j];
     }
 #pragma unroll
     for (int j = 0; j < V; ++j) part[wave][lane * V + j] = lg[j];
@@ -539,64 +609,101 @@ template <int E>
 hipError_t launch_for_e(const GateArgs &a, const GatePlan &p, GateMode final_mode,
                         hipStream_t stream)
 {
-    if (p.n_split == 1) {
-        const int bm = 32 * p.m_blocks;
-        const dim3 grid((a.T + bm - 1) / bm, 1);
+    if (!p.split) {
+        const dim3 grid(p.grid);
+        const dim3 block(64 * 8);
+        // 64 tokens: 8 waves, two per SIMD; 32 tokens: 8 waves, the two of a
+        // pair split every chunk's k
         if (p.m_blocks == 2) {
-            // 64 tokens: 8 waves, two per SIMD
-            const dim3 block(64 * 8);
             if (final_mode == MODE_SELECT)
                 hipLaunchKernelGGL((gate_gemm_kernel<E, 2, 8, MODE_SELECT>), grid, block, 0, stream, a);
             else
                 hipLaunchKernelGGL((gate_gemm_kernel<E, 2, 8, MODE_LOGITS>), grid, block, 0, stream, a);
         } else {
-            // 32 tokens: 8 waves, the two of a pair split every chunk's k
-            const dim3 block(64 * 8);
             if (final_mode == MODE_SELECT)
                 hipLaunchKernelGGL((gate_gemm_kernel<E, 1, 8, MODE_SELECT>), grid, block, 0, stream, a);
             else
                 hipLaunchKernelGGL((gate_gemm_kernel<E, 1, 8, MODE_LOGITS>), grid, block, 0, stream, a);
         }
     } else {
-        const dim3 grid((a.T + 31) / 32, p.n_split);
-        hipLaunchKernelGGL((gate_gemm_kernel<E, 1, 8, MODE_PARTIAL>), grid, dim3(64 * 8), 0, stream, a);
-        const dim3 rgrid(a.T);
-        if (final_mode == MODE_SELECT)
-            hipLaunchKernelGGL((gate_reduce_kernel<E, MODE_SELECT>), rgrid, dim3(RED_NT), 0, stream, a);
+        // split GEMM: 128-expert tiles, 8 waves (two per SIMD): 4 columns of
+        // 32 experts x 2 token halves (64 tokens) or x 2 k-halves (32)
+        const dim3 grid(p.grid), block(64 * 8);
+        if (p.m_blocks == 2)
+            hipLaunchKernelGGL((gate_gemm_kernel<128, 2, 8, MODE_PARTIAL>), grid, block, 0, stream, a);
         else
-            hipLaunchKernelGGL((gate_reduce_kernel<E, MODE_LOGITS>), rgrid, dim3(RED_NT), 0, stream, a);
+            hipLaunchKernelGGL((gate_gemm_kernel<128, 1, 8, MODE_PARTIAL>), grid, block, 0, stream, a);
+        // many slices: 16 waves per token, so that each loads few of them
+        const dim3 rgrid(a.T);
+        if (p.n_split > 16) {
+            if (final_mode == MODE_SELECT)
+                hipLaunchKernelGGL((gate_reduce_kernel<E, MODE_SELECT, 16>), rgrid, dim3(1024), 0, stream, a);
+            else
+                hipLaunchKernelGGL((gate_reduce_kernel<E, MODE_LOGITS, 16>), rgrid, dim3(1024), 0, stream, a);
+        } else {
+            if (final_mode == MODE_SELECT)
+                hipLaunchKernelGGL((gate_reduce_kernel<E, MODE_SELECT, 4>), rgrid, dim3(256), 0, stream, a);
+            else
+                hipLaunchKernelGGL((gate_reduce_kernel<E, MODE_LOGITS, 4>), rgrid, dim3(256), 0, stream, a);
+        }
     }
     return hipGetLastError();
 }
 
 }  // namespace
 
+// Cost model of the split GEMM, in units of one KC-chunk of a 32-token x
+// 128-expert tile on one compute unit (1024 MFMA cycles, about 0.45 us):
+// a workgroup costs (its chunks + SPLIT_LATENCY) x its 32-token blocks,
+// workgroups beyond one per compute unit queue behind it, and the partial
+// logits cross HBM twice (written, then read by the reduction) at about
+// SPLIT_BYTES_PER_UNIT bytes per unit.
+constexpr double SPLIT_LATENCY = 4.0;
+constexpr double SPLIT_BYTES_PER_UNIT = 2.25e6;
+constexpr int N_CU = 256;
+
 GatePlan plan_gate(int T, int d, int E)
 {
-    (void)E;
     GatePlan p{};
     const int chunks = (d + KC - 1) / KC;
     const long tiles64 = ((long)T + 63) / 64;
     const long tiles32 = ((long)T + 31) / 32;
-    // 256 compute units: aim for at least one workgroup each.
-    if (tiles64 >= 256) {
-        p.m_blocks = 2;
-        p.n_split = 1;
-    } else if (tiles32 >= 256) {
-        p.m_blocks = 1;
-        p.n_split = 1;
-    } else {
-        p.m_blocks = 1;
-        long s = tiles32 > 0 ? (256 + tiles32 - 1) / tiles32 : 1;
-        if (s > 64) s = 64;
-        if (s > chunks) s = chunks;
-        if (s < 1) s = 1;
-        const int cps = (int)((chunks + s - 1) / s);
-        p.n_split = (chunks + cps - 1) / cps;
-        p.chunks_per_split = cps;
+    p.n_split = 1;
+    p.chunks_per_split = chunks;
+    p.e_tiles = 1;
+    // Enough 64- or 32-token workgroups for every compute unit: one
+    // workgroup per token tile, all experts, whole k range, fused selection.
+    if (tiles64 >= N_CU || tiles32 >= N_CU) {
+        p.m_blocks = tiles64 >= N_CU ? 2 : 1;
+        p.t_tiles = (int)(p.m_blocks == 2 ? tiles64 : tiles32);
+        p.grid = p.t_tiles;
+        return p;
     }
-    if (p.n_split == 1) p.chunks_per_split = chunks;
-    p.partial_bytes = p.n_split > 1 ? (size_t)p.n_split * (size_t)T * (size_t)E * sizeof(float) : 0;
+    p.split = true;
+    p.e_tiles = E / 128;
+    double best = 1e300;
+    for (int mb = 1; mb <= 2; ++mb) {
+        const long tt = ((long)T + 32 * mb - 1) / (32 * mb);
+        const long tiles = tt * p.e_tiles;
+        for (int s = 1; s <= chunks; ++s) {
+            const int cps = (chunks + s - 1) / s;
+            if ((chunks + cps - 1) / cps != s) continue;   // s slices of cps chunks
+            const long n = tiles * s;
+            const double rounds = (double)((n + N_CU - 1) / N_CU);
+            const double cost = rounds * (cps + SPLIT_LATENCY) * mb +
+                                2.0 * s * (double)T * E * sizeof(float) / SPLIT_BYTES_PER_UNIT;
+            if (cost < best) {
+                best = cost;
+                p.m_blocks = mb;
+                p.t_tiles = (int)tt;
+                p.n_split = s;
+                p.chunks_per_split = cps;
+            }
+        }
+    }
+    const long n = (long)p.t_tiles * p.e_tiles * p.n_split;
+    p.grid = (int)((n + 7) / 8 * 8);
+    p.partial_bytes = (size_t)p.n_split * (size_t)T * (size_t)E * sizeof(float);
     return p;
 }
 

@@ -27,9 +27,12 @@ struct GateArgs {
     int n_group, topk_group, top_k, order;
     int score_func, renorm, mask_zero;
     float route_scale, denom_eps;
+    int E;                  // experts: row length of logits and partials
     int chunks_total;       // ceil(d / KC)
-    int chunks_per_split;   // KC-chunks handled by one blockIdx.y
-    int n_split;            // gridDim.y of the GEMM launch
+    int chunks_per_split;   // KC-chunks of one k-slice
+    int n_split;            // k-slices (1 = whole k range in one workgroup)
+    int t_tiles, e_tiles;   // token and expert tiles of the split GEMM
+    int n_tiles;            // t_tiles * e_tiles * n_split
     float *weights;         // [T, top_k]      (MODE_SELECT)
     int32_t *indices;       // [T, top_k]      (MODE_SELECT)
     float *logits;          // [T, E]          (MODE_LOGITS)
@@ -37,10 +40,18 @@ struct GateArgs {
 };
 
 // How the logits GEMM is cut for a given T.
+//   fused: one workgroup owns 32*m_blocks tokens x all E experts x the whole
+//          k range and runs the selection itself (no partials);
+//   split: one workgroup owns 32*m_blocks tokens x 128 experts x one k-slice
+//          and writes float32 partial logits [n_split, T, E]; a second kernel
+//          adds the slices and runs the selection.
 struct GatePlan {
-    int m_blocks;           // 32-token MFMA blocks per wave: 1 (32 tokens/WG) or 2 (64)
-    int n_split;            // split of the k range; 1 = fused selection epilogue
+    bool split;
+    int m_blocks;           // 32-token MFMA blocks per workgroup: 1 or 2
+    int n_split;            // k-slices (split path)
     int chunks_per_split;
+    int t_tiles, e_tiles;   // split path tiles
+    int grid;               // workgroups of the GEMM launch
     size_t partial_bytes;   // workspace for split partials
 };
 
