@@ -86,10 +86,11 @@ __device__ __forceinline__ float readlane_f(float v, int lane)
 // least 3 * MAX_TOPK words.  Writes row t of weights and indices.
 //
 // The K winners are the K largest choice scores under (v desc, id asc).
-// Scores map to order-preserving uint32 keys; the K-th largest key is found
-// bit by bit from the top (a count of keys >= candidate is one ballot per
-// owned expert), then every key above it is selected and keys equal to it
-// are taken in ascending expert id until K are chosen.
+// Scores map to order-preserving uint32 keys; a threshold is found bit by
+// bit from the top (a count of keys >= candidate is one ballot per owned
+// expert) until it is the K-th largest key or exactly K keys reach it; then
+// every key above it is selected and keys equal to it are taken in
+// ascending expert id until K are chosen.
 template <int V>
 __device__ __forceinline__ void select_token(const float (&lg)[V], const float (&bias_r)[V],
                                              const int lane, const GateArgs &a, const int t,
@@ -167,14 +168,20 @@ __device__ __forceinline__ void select_token(const float (&lg)[V], const float (
 #pragma unroll
     for (int j = 0; j < V; ++j) key[j] = orderable(v[j] + 0.0f);   // -0 -> +0
 
-    // K-th largest key, most significant bit first.
+    // K-th largest key, most significant bit first.  Once exactly K keys
+    // are >= the prefix found so far, those K are the winners and the lower
+    // bits cannot change the choice: stop there (the counts are ballots, so
+    // every lane takes the same branch).
     uint32_t kth = 0;
     for (int b = 31; b >= 0; --b) {
         const uint32_t cand = kth | (1u << b);
         int cnt = 0;
 #pragma unroll
         for (int j = 0; j < V; ++j) cnt += __popcll(__ballot(key[j] >= cand));
-        if (cnt >= K) kth = cand;
+        if (cnt >= K) {
+            kth = cand;
+            if (cnt == K) break;
+        }
     }
 
     // Keys above kth are in; keys equal to kth fill the rest by ascending id
