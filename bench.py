@@ -17,6 +17,12 @@ on the launch stream over the timed steps, against the fp32 MFMA peak.
 WRITE_SIZE, scaled by a plain-copy calibration) when that file was taken
 from the current gate kernel source, else null.
 
+``decode`` reports the decode-size batches (Kimi-K2 T=256, DeepSeek-V3
+T=64): 20 calls captured in one HIP graph and replayed, so the figure is GPU
+time per call without host launch cost; the replayed outputs are checked
+against an eager call.  Their gate roofline is the larger of the fp32 MFMA
+and the HBM time (MFMA binds at both sizes).
+
 ``cpu_baseline`` times the CPU oracle (float64, all host threads) on a
 bounded sample of the same workload.
 """
@@ -162,6 +168,55 @@ class Case:
         return gate_flops, gate_bytes, disp_bytes
 
 
+def decode_line(name: str, calls: int = 20, replays: int = 5):
+    """Gate and gate+dispatch of one decode-size batch, timed by replaying
+    ``calls`` back-to-back calls captured in a HIP graph."""
+    import torch
+    case = Case(name)
+    case.forward()
+    case.dispatch()
+    torch.cuda.synchronize()
+    ref_i = case.indices.clone()
+    ref_p = case.out.perm.clone()
+    ref_x = case.out.permuted_x.clone()
+
+    def per_call(fn):
+        s = torch.cuda.Stream()
+        with torch.cuda.stream(s):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=s):
+                for _ in range(calls):
+                    fn()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(replays):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / (replays * calls)
+
+    gate_us = per_call(case.forward)
+    path_us = per_call(lambda: (case.forward(), case.dispatch()))
+    same = (torch.equal(case.indices, ref_i) and torch.equal(case.out.perm, ref_p)
+            and torch.equal(case.out.permuted_x, ref_x))
+    T = case.w.T
+    flops, gate_bytes, disp_bytes = case.algorithmic()
+    t_mfma = flops / (PEAK_FP32_MFMA_TFLOPS * 1e12) * 1e6
+    t_hbm = gate_bytes / (PEAK_HBM_GBS * 1e9) * 1e6
+    t_roof = max(t_mfma, t_hbm)
+    return {"workload": name, "T": T, "E": case.cfg.E,
+            "gate_us": gate_us, "dispatch_us": path_us - gate_us, "path_us": path_us,
+            "gate_tokens_per_s": T / (gate_us * 1e-6), "path_tokens_per_s": T / (path_us * 1e-6),
+            "gate_bound": "mfma" if t_mfma >= t_hbm else "hbm",
+            "gate_roofline_us": t_roof, "gate_roofline_frac": t_roof / gate_us,
+            "gate_tflops": flops / (gate_us * 1e-6) / 1e12,
+            "gate_algorithmic_GBps": gate_bytes / (gate_us * 1e-6) / 1e9,
+            "graph_replay_matches_eager": bool(same)}
+
+
 def cpu_baseline(case: Case, budget_s: float = 12.0):
     """The oracle, as it stands, on the first n tokens of the workload: gate,
     then dispatch and row gather of those tokens' pairs.  n grows from 256
@@ -203,6 +258,8 @@ def main():
     ap.add_argument("--workload", default="kimi-k2-prefill")
     ap.add_argument("--secondary", default="dsv3-prefill-ties")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true",
+                    help="skip the graph-replayed decode-size lines")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (counter calibration)")
     args = ap.parse_args()
@@ -278,6 +335,8 @@ def main():
             "dispatch_algorithmic_GBps": db2 / (d2 * 1e-3) / 1e9,
         }
         del sec
+    if not args.no_decode:
+        result["decode"] = [decode_line("kimi-k2-decode"), decode_line("dsv3-tiny")]
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(case)
     print(json.dumps(result), flush=True)
