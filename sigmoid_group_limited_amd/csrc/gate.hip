@@ -20,7 +20,7 @@
 //   [BM x KC] (x upcast from bfloat16 to float32 on the way in, exact),
 //   double-buffered, with two more chunks of global loads in flight.
 //   Small batches (fewer than 256 such workgroups) use a split GEMM
-//   instead: a workgroup owns 32 or 64 tokens x 128 experts x one slice of
+//   instead: a workgroup owns 32 tokens x 128 experts x one slice of
 //   the k range and writes float32 partial logits; a second kernel adds the
 //   slices in a fixed order (deterministic) and runs the same selection.
 //   Split tiles are ordered so that the token tiles sharing a W slice run on
@@ -633,13 +633,10 @@ hipError_t launch_for_e(const GateArgs &a, const GatePlan &p, GateMode final_mod
                 hipLaunchKernelGGL((gate_gemm_kernel<E, 1, 8, MODE_LOGITS>), grid, block, 0, stream, a);
         }
     } else {
-        // split GEMM: 128-expert tiles, 8 waves (two per SIMD): 4 columns of
-        // 32 experts x 2 token halves (64 tokens) or x 2 k-halves (32)
+        // split GEMM: 32 tokens x 128 experts, 8 waves (two per SIMD): 4
+        // columns of 32 experts x 2 k-halves of every chunk
         const dim3 grid(p.grid), block(64 * 8);
-        if (p.m_blocks == 2)
-            hipLaunchKernelGGL((gate_gemm_kernel<128, 2, 8, MODE_PARTIAL>), grid, block, 0, stream, a);
-        else
-            hipLaunchKernelGGL((gate_gemm_kernel<128, 1, 8, MODE_PARTIAL>), grid, block, 0, stream, a);
+        hipLaunchKernelGGL((gate_gemm_kernel<128, 1, 8, MODE_PARTIAL>), grid, block, 0, stream, a);
         // many slices: 16 waves per token, so that each loads few of them
         const dim3 rgrid(a.T);
         if (p.n_split > 16) {
@@ -661,10 +658,10 @@ hipError_t launch_for_e(const GateArgs &a, const GatePlan &p, GateMode final_mod
 
 // Cost model of the split GEMM, in units of one KC-chunk of a 32-token x
 // 128-expert tile on one compute unit (1024 MFMA cycles, about 0.45 us):
-// a workgroup costs (its chunks + SPLIT_LATENCY) x its 32-token blocks,
-// workgroups beyond one per compute unit queue behind it, and the partial
-// logits cross HBM twice (written, then read by the reduction) at about
-// SPLIT_BYTES_PER_UNIT bytes per unit.
+// a workgroup costs its chunks + SPLIT_LATENCY, workgroups beyond one per
+// compute unit queue behind it, and the partial logits cross HBM twice
+// (written, then read by the reduction) at about SPLIT_BYTES_PER_UNIT bytes
+// per unit.  (64-token split tiles measured no better overall.)
 constexpr double SPLIT_LATENCY = 4.0;
 constexpr double SPLIT_BYTES_PER_UNIT = 2.25e6;
 constexpr int N_CU = 256;
@@ -687,25 +684,22 @@ GatePlan plan_gate(int T, int d, int E)
         return p;
     }
     p.split = true;
+    p.m_blocks = 1;
+    p.t_tiles = (int)tiles32;
     p.e_tiles = E / 128;
+    const long tiles = tiles32 * p.e_tiles;
     double best = 1e300;
-    for (int mb = 1; mb <= 2; ++mb) {
-        const long tt = ((long)T + 32 * mb - 1) / (32 * mb);
-        const long tiles = tt * p.e_tiles;
-        for (int s = 1; s <= chunks; ++s) {
-            const int cps = (chunks + s - 1) / s;
-            if ((chunks + cps - 1) / cps != s) continue;   // s slices of cps chunks
-            const long n = tiles * s;
-            const double rounds = (double)((n + N_CU - 1) / N_CU);
-            const double cost = rounds * (cps + SPLIT_LATENCY) * mb +
-                                2.0 * s * (double)T * E * sizeof(float) / SPLIT_BYTES_PER_UNIT;
-            if (cost < best) {
-                best = cost;
-                p.m_blocks = mb;
-                p.t_tiles = (int)tt;
-                p.n_split = s;
-                p.chunks_per_split = cps;
-            }
+    for (int s = 1; s <= chunks; ++s) {
+        const int cps = (chunks + s - 1) / s;
+        if ((chunks + cps - 1) / cps != s) continue;   // s slices of cps chunks
+        const long n = tiles * s;
+        const double rounds = (double)((n + N_CU - 1) / N_CU);
+        const double cost = rounds * (cps + SPLIT_LATENCY) +
+                            2.0 * s * (double)T * E * sizeof(float) / SPLIT_BYTES_PER_UNIT;
+        if (cost < best) {
+            best = cost;
+            p.n_split = s;
+            p.chunks_per_split = cps;
         }
     }
     const long n = (long)p.t_tiles * p.e_tiles * p.n_split;

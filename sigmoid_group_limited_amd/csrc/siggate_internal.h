@@ -42,12 +42,12 @@ struct GateArgs {
 // How the logits GEMM is cut for a given T.
 //   fused: one workgroup owns 32*m_blocks tokens x all E experts x the whole
 //          k range and runs the selection itself (no partials);
-//   split: one workgroup owns 32*m_blocks tokens x 128 experts x one k-slice
+//   split: one workgroup owns 32 tokens x 128 experts x one k-slice
 //          and writes float32 partial logits [n_split, T, E]; a second kernel
 //          adds the slices and runs the selection.
 struct GatePlan {
     bool split;
-    int m_blocks;           // 32-token MFMA blocks per workgroup: 1 or 2
+    int m_blocks;           // 32-token blocks per workgroup: 1 or 2 (fused), 1 (split)
     int n_split;            // k-slices (split path)
     int chunks_per_split;
     int t_tiles, e_tiles;   // split path tiles

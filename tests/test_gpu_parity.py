@@ -100,6 +100,31 @@ def test_gate_parity_small(o, name, gc, T, d, order):
     say(f"    {stats}")
 
 
+# Batch sizes across the small-batch plan at d=7168: k-slice counts from 112
+# down to 1 (expert tiles only), 4 and 16 reduction waves, grids padded to a
+# multiple of 8, ragged last token tiles; and both fused tile heights.
+PLAN_SWEEP = [(2, 256), (33, 384), (65, 256), (129, 384), (300, 256), (511, 384),
+              (1000, 256), (2047, 384), (4000, 256), (6000, 384), (8191, 256), (12000, 384)]
+
+
+@pytest.mark.parametrize("T,E", PLAN_SWEEP, ids=[f"T{t}_E{e}" for t, e in PLAN_SWEEP])
+def test_gate_plan_sweep(o, T, E):
+    """Full-width d over the batch sizes where the GEMM plan changes; the
+    oracle on sampled tokens (first, last and random), properties on all."""
+    gc = wl.DSV3 if E == 256 else wl.KIMI_K2
+    d = 7168
+    say(f"[plan] T={T} E={E}")
+    gi = wl.make_gate_inputs(T, d, gc, seed=T * 7 + E)
+    cfg = cfg_of(gc, T, d)
+    w, i = run_gate(gi, cfg)
+    check_rows_valid(i, gc.n_experts, gc.n_group, gc.topk_group)
+    rng = np.random.default_rng(T)
+    rows = np.arange(T) if T <= 300 else np.unique(np.r_[0, 31, 32, T - 1, rng.integers(0, T, 200)])
+    ref = oracle_gate(o, gi, cfg, rows)
+    stats = compare_gate(w, i, ref, gc.route_scale, rows)
+    say(f"    {stats}")
+
+
 @pytest.mark.parametrize("T,E,d", [(100, 256, 7168), (16384, 384, 96), (9000, 128, 40)])
 def test_logits_exact_on_integer_inputs(o, T, E, d):
     """x small integers, W integers times 2^-8: every partial sum is exact in
@@ -229,6 +254,9 @@ def test_deterministic_repeat():
     (0, 8, 256, 64, False), (1, 8, 256, 64, False), (255, 8, 256, 128, False),
     (257, 8, 384, 64, False), (1000, 3, 7, 24, False), (513, 1, 16, 8, False),
     (70000, 8, 256, 16, True), (4097, 8, 384, 7168, False),
+    # the one-launch small path up to exactly 4096 pairs, and just past it
+    (512, 8, 384, 7168, False), (512, 8, 256, 7168, True), (4096, 1, 128, 40, False),
+    (4097, 1, 128, 40, False), (2, 8, 384, 8, False), (64, 8, 256, 7168, True),
 ])
 def test_dispatch_parity(o, T, K, E, d, hot):
     say(f"[dispatch] T={T} K={K} E={E} d={d} hot={hot}")
