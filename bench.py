@@ -17,6 +17,10 @@ on the launch stream over the timed steps, against the fp32 MFMA peak.
 WRITE_SIZE, scaled by a plain-copy calibration) when that file was taken
 from the current gate kernel source, else null.
 
+``stages`` also carries the medians of the per-step event times, and
+``cold`` the medians of steps that each follow a 1 GiB scrub write (x and W
+then come from HBM, not the 256 MB Infinity Cache).
+
 ``decode`` reports the decode-size batches (Kimi-K2 T=256, DeepSeek-V3
 T=64): 20 calls captured in one HIP graph and replayed, so the figure is GPU
 time per call without host launch cost; the replayed outputs are checked
@@ -127,9 +131,29 @@ class Case:
             ev[i][2].record()
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
-        gate_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
-        disp_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
-        return wall / steps * 1e3, gate_ms, disp_ms
+        g = [e[0].elapsed_time(e[1]) for e in ev]
+        dd = [e[1].elapsed_time(e[2]) for e in ev]
+        self.medians = (float(np.median(g)), float(np.median(dd)))
+        return wall / steps * 1e3, float(np.mean(g)), float(np.mean(dd))
+
+    def run_cold(self, steps: int):
+        """Each step after writing a 1 GiB scrub buffer (larger than the
+        256 MB Infinity Cache), so x and W come from HBM; gate and dispatch
+        timed with HIP events.  Returns medians in ms."""
+        import torch
+        scrub = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+        for i in range(steps):
+            scrub.fill_(i & 0xff)
+            ev[i][0].record()
+            self.forward()
+            ev[i][1].record()
+            self.dispatch()
+            ev[i][2].record()
+        torch.cuda.synchronize()
+        del scrub
+        return (float(np.median([e[0].elapsed_time(e[1]) for e in ev])),
+                float(np.median([e[1].elapsed_time(e[2]) for e in ev])))
 
     def run_next_rows(self, steps: int, warmup: int):
         """Times the steps after the path, on this workload's own outputs:
@@ -260,6 +284,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true",
                     help="skip the graph-replayed decode-size lines")
+    ap.add_argument("--no-cold", action="store_true", help="skip the scrubbed (cold) steps")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (counter calibration)")
     args = ap.parse_args()
@@ -322,6 +347,12 @@ def main():
         },
     }
     result["stages"]["path_roofline_frac"] = result["value"] / result["stages"]["roofline_tokens_per_s"]
+    result["stages"]["gate_ms_median"], result["stages"]["dispatch_ms_median"] = case.medians
+    if not args.no_cold:
+        cg, cd = case.run_cold(max(5, args.steps // 2))
+        result["cold"] = {"gate_ms_median": cg, "dispatch_ms_median": cd,
+                          "tokens_per_s": T / ((cg + cd) * 1e-3),
+                          "note": "1 GiB scrub written before each step"}
     result["after_path"] = case.run_next_rows(max(3, args.steps // 2), 2)
     if args.secondary:
         sec = Case(args.secondary)
