@@ -37,6 +37,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int KPAD = KC + 4;    // padded LDS row in floats: rows start 4 banks apart
+constexpr int SPLIT_STAGES = 4; // chunks of global loads in flight in the split GEMM
 
 // Workgroup of NW waves: 4 expert quarters x WM token splits x KS k-splits.
 // A k-split wave pair shares a tile and processes alternate halves of every
@@ -308,7 +309,7 @@ __device__ __forceinline__ void finish_tile(const GateArgs &a,
     }
 }
 
-template <int E, int MB, int NW, int MODE>
+template <int E, int MB, int NW, int MODE, int P>
 __global__ __launch_bounds__(64 * NW) void gate_gemm_kernel(GateArgs a)
 {
     using S = Shape<E, MB, NW>;
@@ -448,27 +449,29 @@ __global__ __launch_bounds__(64 * NW) void gate_gemm_kernel(GateArgs a)
     static_assert(KC == 32, "the step below is written for four 8-column groups");
 
     // Pipeline over KC-column chunks.  While chunk c feeds the matrix cores
-    // from one LDS buffer, chunks c+1 and c+2 wait in two register stages.
+    // from one LDS buffer, chunks c+1 .. c+P wait in P register stages.
     // After the first 8-column group of chunk c, chunk c+1 is written to the
-    // other LDS buffer and its register stage is refilled with chunk c+3, so
-    // every global load has two chunks of MFMA work to land in.  The one
-    // barrier per chunk comes once the last fragments of chunk c are in
-    // registers: the MFMAs of that last group then cover the LDS latency of
-    // the first fragments of chunk c+1.  The stages alternate, so the loop
-    // handles chunks in pairs (static indices).  Past the last chunk, loads
+    // other LDS buffer and its register stage is refilled with chunk c+1+P,
+    // so every global load has P chunks of MFMA work to land in (P = 2 for
+    // the long fused tiles; more for the short split tiles, whose chunks are
+    // a sixth as long).  The one barrier per chunk comes once the last
+    // fragments of chunk c are in registers: the MFMAs of that last group
+    // then cover the LDS latency of the first fragments of chunk c+1.  Local
+    // chunk i uses LDS buffer i%2 and stage (i+1)%P, so the loop is unrolled
+    // by lcm(P, 2) to keep both indices static.  Past the last chunk, loads
     // and stores repeat the last chunk (never read) instead of branching.
     if (c_begin < c_end) {
         const int c_last = c_end - 1;
-        Stage stA, stB;
+        Stage st[P];
         Frag f, g;
         // this wave's 8-column groups of every chunk: g0 .. g0 + 4/KS - 1
         const int g0 = wk * (4 / S::KS);
-        auto step = [&](int c, int buf, Stage &st) {
-            // f holds group g0 of chunk c
+        auto step = [&](int c, int buf, Stage &sg) {
+            // f holds group g0 of chunk c; sg holds chunk c+1
             read_frag(buf, g0 + 1, g);
             mma(f);
-            store_lds(min(c + 1, c_last), buf ^ 1, st);
-            load_global(min(c + 3, c_last), st);
+            store_lds(min(c + 1, c_last), buf ^ 1, sg);
+            load_global(min(c + 1 + P, c_last), sg);
             if constexpr (S::KS == 1) {
                 read_frag(buf, 2, f);
                 mma(g);
@@ -483,18 +486,22 @@ __global__ __launch_bounds__(64 * NW) void gate_gemm_kernel(GateArgs a)
             read_frag(buf ^ 1, g0, f);   // first group of chunk c+1
             mma(g);
         };
-        load_global(c_begin, stA);
-        load_global(min(c_begin + 1, c_last), stB);
-        store_lds(c_begin, 0, stA);
-        load_global(min(c_begin + 2, c_last), stA);
+        load_global(c_begin, st[0]);
+#pragma unroll
+        for (int j = 1; j < P; ++j) load_global(min(c_begin + j, c_last), st[j]);
+        store_lds(c_begin, 0, st[0]);
+        load_global(min(c_begin + P, c_last), st[0]);
         __syncthreads();
         read_frag(0, g0, f);
+        constexpr int U = P % 2 ? 2 * P : P;
         int c = c_begin;
-        for (; c + 1 < c_end; c += 2) {
-            step(c, 0, stB);        // stores chunk c+1 (stB), refills stB with c+3
-            step(c + 1, 1, stA);    // stores chunk c+2 (stA), refills stA with c+4
+        for (; c + U <= c_end; c += U) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) step(c + u, u & 1, st[(u + 1) % P]);
         }
-        if (c < c_end) step(c, 0, stB);
+#pragma unroll
+        for (int u = 0; u < U - 1; ++u)
+            if (c + u < c_end) step(c + u, u & 1, st[(u + 1) % P]);
         __syncthreads();   // every wave is done with the staging buffers
     }
 
@@ -623,20 +630,20 @@ hipError_t launch_for_e(const GateArgs &a, const GatePlan &p, GateMode final_mod
         // pair split every chunk's k
         if (p.m_blocks == 2) {
             if (final_mode == MODE_SELECT)
-                hipLaunchKernelGGL((gate_gemm_kernel<E, 2, 8, MODE_SELECT>), grid, block, 0, stream, a);
+                hipLaunchKernelGGL((gate_gemm_kernel<E, 2, 8, MODE_SELECT, 2>), grid, block, 0, stream, a);
             else
-                hipLaunchKernelGGL((gate_gemm_kernel<E, 2, 8, MODE_LOGITS>), grid, block, 0, stream, a);
+                hipLaunchKernelGGL((gate_gemm_kernel<E, 2, 8, MODE_LOGITS, 2>), grid, block, 0, stream, a);
         } else {
             if (final_mode == MODE_SELECT)
-                hipLaunchKernelGGL((gate_gemm_kernel<E, 1, 8, MODE_SELECT>), grid, block, 0, stream, a);
+                hipLaunchKernelGGL((gate_gemm_kernel<E, 1, 8, MODE_SELECT, 2>), grid, block, 0, stream, a);
             else
-                hipLaunchKernelGGL((gate_gemm_kernel<E, 1, 8, MODE_LOGITS>), grid, block, 0, stream, a);
+                hipLaunchKernelGGL((gate_gemm_kernel<E, 1, 8, MODE_LOGITS, 2>), grid, block, 0, stream, a);
         }
     } else {
         // split GEMM: 32 tokens x 128 experts, 8 waves (two per SIMD): 4
         // columns of 32 experts x 2 k-halves of every chunk
         const dim3 grid(p.grid), block(64 * 8);
-        hipLaunchKernelGGL((gate_gemm_kernel<128, 1, 8, MODE_PARTIAL>), grid, block, 0, stream, a);
+        hipLaunchKernelGGL((gate_gemm_kernel<128, 1, 8, MODE_PARTIAL, SPLIT_STAGES>), grid, block, 0, stream, a);
         // many slices: 16 waves per token, so that each loads few of them
         const dim3 rgrid(a.T);
         if (p.n_split > 16) {
