@@ -466,6 +466,46 @@ __global__ __launch_bounds__(64 * NW) void gate_gemm_kernel(GateArgs a)
         Frag f, g;
         // this wave's 8-column groups of every chunk: g0 .. g0 + 4/KS - 1
         const int g0 = wk * (4 / S::KS);
+        // Issue order inside a step (one wave, KS == 1): one memory
+        // operation after each MFMA, so no group waits on its fragments and
+        // the LDS stores and global loads hide under matrix work.  Groups
+        // 0..2 of the chunk run before the barrier: group 0 alongside the
+        // fragment reads of group 1 and the LDS stores of chunk c+1, group 1
+        // alongside the global loads of chunk c+1+P and the reads of group
+        // 2, group 2 alongside the reads of group 3; group 3 runs after the
+        // barrier alongside the reads of the next chunk's group 0.
+        constexpr int NMG = 4 * S::MBW * S::NB;               // MFMAs per group
+        constexpr int NRG = S::MBW + S::NB;                   // fragment reads per group
+        constexpr int NWR = WLOADS + (XE >= 4 ? XE / 4 : 1);  // LDS stores per chunk
+        constexpr int NVM = WLOADS + 1;                       // global loads per chunk
+        constexpr int SG_MFMA = 0x008, SG_VMEM_READ = 0x020, SG_DS_READ = 0x100,
+                      SG_DS_WRITE = 0x200;
+        auto interleave_body = [&]() {
+#pragma unroll
+            for (int i = 0; i < NMG; ++i) {
+                __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+                if (i < NRG) __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 1, 0);
+                else if (i - NRG < NWR) __builtin_amdgcn_sched_group_barrier(SG_DS_WRITE, 1, 0);
+            }
+#pragma unroll
+            for (int i = 0; i < NMG; ++i) {
+                __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+                if (i < NVM) __builtin_amdgcn_sched_group_barrier(SG_VMEM_READ, 1, 0);
+                else if (i - NVM < NRG) __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 1, 0);
+            }
+#pragma unroll
+            for (int i = 0; i < NMG; ++i) {
+                __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+                if (i < NRG) __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 1, 0);
+            }
+        };
+        auto interleave_tail = [&]() {
+#pragma unroll
+            for (int i = 0; i < NMG; ++i) {
+                __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+                if (i < NRG) __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 1, 0);
+            }
+        };
         auto step = [&](int c, int buf, Stage &sg) {
             // f holds group g0 of chunk c; sg holds chunk c+1
             read_frag(buf, g0 + 1, g);
@@ -477,6 +517,7 @@ __global__ __launch_bounds__(64 * NW) void gate_gemm_kernel(GateArgs a)
                 mma(g);
                 read_frag(buf, 3, g);
                 mma(f);
+                interleave_body();
             }
             // keep the last group's MFMAs after the barrier (the scheduler
             // would otherwise hoist them and expose the LDS latency below)
@@ -485,6 +526,7 @@ __global__ __launch_bounds__(64 * NW) void gate_gemm_kernel(GateArgs a)
             __builtin_amdgcn_sched_barrier(0);
             read_frag(buf ^ 1, g0, f);   // first group of chunk c+1
             mma(g);
+            if constexpr (S::KS == 1) interleave_tail();
         };
         load_global(c_begin, st[0]);
 #pragma unroll
