@@ -499,6 +499,23 @@ __global__ __launch_bounds__(64 * NW) void gate_gemm_kernel(GateArgs a)
                 if (i < NRG) __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 1, 0);
             }
         };
+        // k-split pair (KS == 2): each wave has one group before the barrier;
+        // its MFMAs carry the reads of the wave's second group, the LDS
+        // stores and the global loads, spread evenly.
+        auto interleave_split = [&]() {
+            constexpr int OPS = NRG + NWR + NVM;
+            constexpr int PER = (OPS + NMG - 1) / NMG;
+#pragma unroll
+            for (int i = 0; i < NMG; ++i) {
+                __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+#pragma unroll
+                for (int k = i * PER; k < (i + 1) * PER && k < OPS; ++k) {
+                    if (k < NRG) __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 1, 0);
+                    else if (k < NRG + NWR) __builtin_amdgcn_sched_group_barrier(SG_DS_WRITE, 1, 0);
+                    else __builtin_amdgcn_sched_group_barrier(SG_VMEM_READ, 1, 0);
+                }
+            }
+        };
         auto interleave_tail = [&]() {
 #pragma unroll
             for (int i = 0; i < NMG; ++i) {
@@ -518,6 +535,8 @@ __global__ __launch_bounds__(64 * NW) void gate_gemm_kernel(GateArgs a)
                 read_frag(buf, 3, g);
                 mma(f);
                 interleave_body();
+            } else {
+                interleave_split();
             }
             // keep the last group's MFMAs after the barrier (the scheduler
             // would otherwise hoist them and expose the LDS latency below)
@@ -526,7 +545,7 @@ __global__ __launch_bounds__(64 * NW) void gate_gemm_kernel(GateArgs a)
             __builtin_amdgcn_sched_barrier(0);
             read_frag(buf ^ 1, g0, f);   // first group of chunk c+1
             mma(g);
-            if constexpr (S::KS == 1) interleave_tail();
+            interleave_tail();
         };
         load_global(c_begin, st[0]);
 #pragma unroll
