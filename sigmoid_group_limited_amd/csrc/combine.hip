@@ -9,9 +9,9 @@
 // Here the products are rounded to float32 and summed in ascending k, and
 // the result is rounded to bfloat16 (nearest even).
 //
-// One block per token: each thread owns 8 columns (16 bytes), reads the K
-// source rows at dest[] and writes one row.  HBM-bound: K*2d bytes read and
-// 2d written per token.
+// One block per token: each thread owns 8-column (16-byte) vectors, reads
+// the K source rows at dest[] and writes one row.  HBM-bound: K*2d bytes read
+// and 2d written per token.
 #include "siggate_internal.h"
 
 namespace siggate {
@@ -29,39 +29,57 @@ __device__ __forceinline__ unsigned bf16_rne(float f)
     return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
 
+// K (top_k) is a template parameter so that every slot's load is issued
+// before any is used: the loads of a pass do not wait on each other.  A slot
+// whose dest is out of range reads row 0 instead and is masked out of the
+// sum (the same arithmetic as skipping it).  Each thread handles two column
+// vectors per pass, so 2K loads are in flight.
+template <int K>
 __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a)
 {
     const int t = blockIdx.x;
-    const int K = a.top_k;
     const long npos = (long)a.T * K;
-    int src[MAX_TOPK];
-    float w[MAX_TOPK];
+    const u32x4 *rows[K];
+    bool ok[K];
+    float w[K];
 #pragma unroll
-    for (int k = 0; k < MAX_TOPK; ++k) {
-        const int p = k < K ? a.dest[(size_t)t * K + k] : -1;
-        src[k] = (p >= 0 && p < npos) ? p : -1;
-        w[k] = k < K ? a.weights[(size_t)t * K + k] : 0.0f;
+    for (int k = 0; k < K; ++k) {
+        const int p = a.dest[(size_t)t * K + k];
+        ok[k] = p >= 0 && p < npos;
+        rows[k] = (const u32x4 *)(a.expert_out + (size_t)(ok[k] ? p : 0) * a.d);
+        w[k] = a.weights[(size_t)t * K + k];
     }
     const int nvec = a.d / 8;
     u32x4 *yrow = (u32x4 *)(a.y + (size_t)t * a.d);
-    for (int i = threadIdx.x; i < nvec; i += blockDim.x) {
-        float acc[8];
+    for (int i0 = threadIdx.x; i0 < nvec; i0 += 2 * 256) {
+        const int i1 = i0 + 256;
+        const int j1 = min(i1, nvec - 1);   // in range; stored only if i1 is
+        u32x4 v[2][K];
 #pragma unroll
-        for (int q = 0; q < 8; ++q) acc[q] = 0.0f;
-#pragma unroll
-        for (int k = 0; k < MAX_TOPK; ++k) {
-            if (src[k] < 0) continue;
-            const u32x4 v = ((const u32x4 *)(a.expert_out + (size_t)src[k] * a.d))[i];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                acc[2 * q] = __fadd_rn(acc[2 * q], __fmul_rn(w[k], bf16_lo(v[q])));
-                acc[2 * q + 1] = __fadd_rn(acc[2 * q + 1], __fmul_rn(w[k], bf16_hi(v[q])));
-            }
+        for (int k = 0; k < K; ++k) {
+            v[0][k] = rows[k][i0];
+            v[1][k] = rows[k][j1];
         }
-        u32x4 o;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) o[q] = bf16_rne(acc[2 * q]) | (bf16_rne(acc[2 * q + 1]) << 16);
-        yrow[i] = o;
+        for (int h = 0; h < 2; ++h) {
+            float acc[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) acc[q] = 0.0f;
+#pragma unroll
+            for (int k = 0; k < K; ++k)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const float lo = __fadd_rn(acc[2 * q], __fmul_rn(w[k], bf16_lo(v[h][k][q])));
+                    const float hi = __fadd_rn(acc[2 * q + 1], __fmul_rn(w[k], bf16_hi(v[h][k][q])));
+                    acc[2 * q] = ok[k] ? lo : acc[2 * q];
+                    acc[2 * q + 1] = ok[k] ? hi : acc[2 * q + 1];
+                }
+            u32x4 o;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) o[q] = bf16_rne(acc[2 * q]) | (bf16_rne(acc[2 * q + 1]) << 16);
+            if (h == 0) yrow[i0] = o;
+            else if (i1 < nvec) yrow[i1] = o;
+        }
     }
 }
 
@@ -69,7 +87,19 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a)
 
 hipError_t launch_combine(const CombineArgs &a, hipStream_t stream)
 {
-    if (a.T > 0) hipLaunchKernelGGL(combine_kernel, dim3(a.T), dim3(256), 0, stream, a);
+    if (a.T == 0) return hipSuccess;
+    const dim3 grid(a.T), block(256);
+    switch (a.top_k) {
+    case 1: hipLaunchKernelGGL(combine_kernel<1>, grid, block, 0, stream, a); break;
+    case 2: hipLaunchKernelGGL(combine_kernel<2>, grid, block, 0, stream, a); break;
+    case 3: hipLaunchKernelGGL(combine_kernel<3>, grid, block, 0, stream, a); break;
+    case 4: hipLaunchKernelGGL(combine_kernel<4>, grid, block, 0, stream, a); break;
+    case 5: hipLaunchKernelGGL(combine_kernel<5>, grid, block, 0, stream, a); break;
+    case 6: hipLaunchKernelGGL(combine_kernel<6>, grid, block, 0, stream, a); break;
+    case 7: hipLaunchKernelGGL(combine_kernel<7>, grid, block, 0, stream, a); break;
+    case 8: hipLaunchKernelGGL(combine_kernel<8>, grid, block, 0, stream, a); break;
+    default: return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 

@@ -150,3 +150,31 @@ def test_combine_full_size(o):
     tol = combine_tolerance(o, sub_out, w64, local, y64, K)
     assert np.all(np.abs(got - y64) <= tol)
     assert (got16 != want16).mean() < 1e-2
+
+
+@pytest.mark.parametrize("K,d", [(3, 40), (5, 7168), (1, 264), (8, 1032)])
+def test_combine_slots_and_skips(o, K, d):
+    """Every top_k from one template, row widths that leave a ragged last
+    pass, and dest entries out of range (-1 or >= n_pos), which contribute
+    nothing; the oracle sees those slots as weight 0 on a valid row."""
+    T = 300
+    say(f"[combine] K={K} d={d}")
+    rng = np.random.default_rng(K * 1000 + d)
+    n_pos = T * K
+    dest = rng.permutation(n_pos).astype(np.int32)
+    skip = rng.random(n_pos) < 0.1
+    dest_gpu = dest.copy()
+    dest_gpu[skip] = np.where(rng.random(int(skip.sum())) < 0.5, -1, n_pos + 7)
+    wts = rng.uniform(0.0, 0.7, size=(T, K)).astype(np.float32)
+    outs = wl.bf16_bits(rng.standard_normal((n_pos, d), dtype=np.float32))
+    cfg = sg.Cfg(T, d, 8, 1, 1, K, 1.0)
+    y = sg.siggate_combine(torch.from_numpy(outs.view(np.int16)).cuda().view(torch.bfloat16),
+                           torch.from_numpy(wts).cuda(), torch.from_numpy(dest_gpu).cuda(), cfg)
+    torch.cuda.synchronize()
+    got16 = y.view(torch.int16).cpu().numpy().view(np.uint16)
+    w64 = wts.astype(np.float64)
+    w64[skip.reshape(T, K)] = 0.0
+    y64, want16 = o.combine(outs, w64, dest)
+    got = wl.bf16_to_f32(got16).astype(np.float64)
+    assert np.all(np.abs(got - y64) <= combine_tolerance(o, outs, w64, dest, y64, K))
+    assert (got16 != want16).mean() < 1e-2
