@@ -64,6 +64,8 @@ SMALL = [
     ("dsv3_fused32_T8229_d256", wl.DSV3, 8229, 256),
     ("kimi_fused64_T16389_d256", wl.KIMI_K2, 16389, 256),
     ("dsv3_fused64_T16447_d200", wl.DSV3, 16447, 200),
+    ("e128_g4_fused64_T16400_d96", wl.GateConfig(128, 4, 2, 6, 1.0), 16400, 96),
+    ("e128_g1_fused32_T9000_d136", wl.GateConfig(128, 1, 1, 8, 2.5), 9000, 136),
 ]
 
 
