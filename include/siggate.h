@@ -87,8 +87,9 @@ typedef enum siggate_status {
 } siggate_status_t;
 
 /* Bytes of device workspace that siggate_forward and siggate_dispatch need
- * for this configuration (the larger of the two; 0 is possible).  Returns 0
- * for a configuration that either call would reject. */
+ * for this configuration: the larger of the two needs, counting only a call
+ * that accepts the configuration (0 if neither does; 0 is also possible for
+ * an accepted configuration). */
 size_t siggate_workspace_bytes(const siggate_cfg_t *cfg);
 
 /* Gate.
