@@ -251,12 +251,17 @@ def cpu_baseline(case: Case, budget_s: float = 12.0):
     c = case.cfg
     gi = case.gi
 
+    split = {}
+
     def one(n):
         t0 = time.perf_counter()
         r = o.gate(gi.x[:n], gi.W, gi.bias, c.n_group, c.topk_group, c.top_k, c.route_scale)
+        t1 = time.perf_counter()
         dr = o.dispatch(r.indices, c.E)
         o.gather_rows(gi.x[:n], dr.perm, c.top_k)
-        return time.perf_counter() - t0
+        t2 = time.perf_counter()
+        split["gate"], split["dispatch"] = t1 - t0, t2 - t1
+        return t2 - t0
 
     n = 256
     dt = one(n)
@@ -270,6 +275,8 @@ def cpu_baseline(case: Case, budget_s: float = 12.0):
             n = n_final
             dt = one(n)
     return dict(value=n / dt, unit="tokens/s", cores=o.num_threads(), kind="oracle",
+                gate_tokens_per_s=n / split["gate"],
+                dispatch_tokens_per_s=n / split["dispatch"],
                 sample=f"first {n} of {case.w.T} tokens of {case.w.name}: float64 gate, "
                        f"dispatch and row gather of their {n * c.top_k} pairs; {dt:.2f} s")
 
