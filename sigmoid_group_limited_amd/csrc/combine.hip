@@ -92,17 +92,16 @@ hipError_t launch_combine(const CombineArgs &a, hipStream_t stream)
     if (a.T == 0) return hipSuccess;
     const dim3 grid(a.T), block(256);
     switch (a.top_k) {
-    case 1: hipLaunchKernelGGL(combine_kernel<1>, grid, block, 0, stream, a); break;
-    case 2: hipLaunchKernelGGL(combine_kernel<2>, grid, block, 0, stream, a); break;
-    case 3: hipLaunchKernelGGL(combine_kernel<3>, grid, block, 0, stream, a); break;
-    case 4: hipLaunchKernelGGL(combine_kernel<4>, grid, block, 0, stream, a); break;
-    case 5: hipLaunchKernelGGL(combine_kernel<5>, grid, block, 0, stream, a); break;
-    case 6: hipLaunchKernelGGL(combine_kernel<6>, grid, block, 0, stream, a); break;
-    case 7: hipLaunchKernelGGL(combine_kernel<7>, grid, block, 0, stream, a); break;
-    case 8: hipLaunchKernelGGL(combine_kernel<8>, grid, block, 0, stream, a); break;
+    case 1: return launch_kernel(combine_kernel<1>, grid, block, stream, a);
+    case 2: return launch_kernel(combine_kernel<2>, grid, block, stream, a);
+    case 3: return launch_kernel(combine_kernel<3>, grid, block, stream, a);
+    case 4: return launch_kernel(combine_kernel<4>, grid, block, stream, a);
+    case 5: return launch_kernel(combine_kernel<5>, grid, block, stream, a);
+    case 6: return launch_kernel(combine_kernel<6>, grid, block, stream, a);
+    case 7: return launch_kernel(combine_kernel<7>, grid, block, stream, a);
+    case 8: return launch_kernel(combine_kernel<8>, grid, block, stream, a);
     default: return hipErrorInvalidValue;
     }
-    return hipGetLastError();
 }
 
 }  // namespace siggate

@@ -306,35 +306,26 @@ size_t dispatch_workspace_bytes(int T, int E, int top_k, bool need_dest)
 
 hipError_t launch_dispatch_meta(const DispatchArgs &a, hipStream_t stream)
 {
-    if (a.n_blocks == 0) {
-        hipLaunchKernelGGL(dispatch_zero_kernel, dim3(1), dim3(BT), 0, stream, a);
-        return hipGetLastError();
-    }
-    hipLaunchKernelGGL(dispatch_count_kernel, dim3(a.n_blocks), dim3(BT), 0, stream, a);
-    hipLaunchKernelGGL(dispatch_scan_kernel, dim3(a.E), dim3(SCAN_THREADS), 0, stream, a);
-    hipLaunchKernelGGL(dispatch_scatter_kernel, dim3(a.n_blocks), dim3(BT), 0, stream, a);
-    return hipGetLastError();
+    if (a.n_blocks == 0) return launch_kernel(dispatch_zero_kernel, dim3(1), dim3(BT), stream, a);
+    hipError_t e = launch_kernel(dispatch_count_kernel, dim3(a.n_blocks), dim3(BT), stream, a);
+    if (e == hipSuccess) e = launch_kernel(dispatch_scan_kernel, dim3(a.E), dim3(SCAN_THREADS), stream, a);
+    if (e == hipSuccess) e = launch_kernel(dispatch_scatter_kernel, dim3(a.n_blocks), dim3(BT), stream, a);
+    return e;
 }
 
 hipError_t launch_dispatch(const DispatchArgs &a, hipStream_t stream)
 {
-    if (a.n_blocks == 0) {
-        hipLaunchKernelGGL(dispatch_zero_kernel, dim3(1), dim3(BT), 0, stream, a);
-        return hipGetLastError();
-    }
+    if (a.n_blocks == 0) return launch_kernel(dispatch_zero_kernel, dim3(1), dim3(BT), stream, a);
     if ((long)a.T * a.top_k <= SMALL_PAIRS) {
         // split each row over enough blocks to reach about 256 of them
         int parts = 1;
         while ((long)a.T * parts * 2 <= 256 && parts * 2 <= a.d / 8) parts *= 2;
-        hipLaunchKernelGGL(dispatch_small_kernel, dim3(a.T * parts), dim3(SMALL_NT), 0, stream, a,
-                           parts);
-        return hipGetLastError();
+        return launch_kernel(dispatch_small_kernel, dim3(a.T * parts), dim3(SMALL_NT), stream, a,
+                             parts);
     }
-    hipLaunchKernelGGL(dispatch_count_kernel, dim3(a.n_blocks), dim3(BT), 0, stream, a);
-    hipLaunchKernelGGL(dispatch_scan_kernel, dim3(a.E), dim3(SCAN_THREADS), 0, stream, a);
-    hipLaunchKernelGGL(dispatch_scatter_kernel, dim3(a.n_blocks), dim3(BT), 0, stream, a);
-    hipLaunchKernelGGL(dispatch_gather_kernel, dim3(a.T), dim3(256), 0, stream, a);
-    return hipGetLastError();
+    hipError_t e = launch_dispatch_meta(a, stream);
+    if (e == hipSuccess) e = launch_kernel(dispatch_gather_kernel, dim3(a.T), dim3(256), stream, a);
+    return e;
 }
 
 }  // namespace siggate

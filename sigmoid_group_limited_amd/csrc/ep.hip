@@ -140,34 +140,29 @@ __global__ __launch_bounds__(NT) void ep_dedup_finish_kernel(EpDedupArgs a)
 hipError_t launch_ep_send_splits(const int32_t *tpe, int E, int ep_size, int32_t *counts,
                                  int32_t *offsets, hipStream_t stream)
 {
-    hipLaunchKernelGGL(ep_send_splits_kernel, dim3(1), dim3(NT), 0, stream, tpe, E, ep_size,
-                       counts, offsets);
-    return hipGetLastError();
+    return launch_kernel(ep_send_splits_kernel, dim3(1), dim3(NT), stream, tpe, E, ep_size,
+                         counts, offsets);
 }
 
 hipError_t launch_ep_regroup(const int32_t *counts, int ep_size, int per, int capacity,
                              int32_t *local_counts, int32_t *regroup, hipStream_t stream)
 {
-    hipLaunchKernelGGL(ep_regroup_kernel, dim3(ep_size * per), dim3(NT), 0, stream, counts,
-                       ep_size, per, capacity, local_counts, regroup);
-    return hipGetLastError();
+    return launch_kernel(ep_regroup_kernel, dim3(ep_size * per), dim3(NT), stream, counts,
+                         ep_size, per, capacity, local_counts, regroup);
 }
 
 hipError_t launch_ep_dedup_map(const EpDedupArgs &a, hipStream_t stream)
 {
-    if (a.T > 0)
-        hipLaunchKernelGGL(ep_dedup_map_kernel, dim3((a.T + NT - 1) / NT), dim3(NT), 0, stream, a);
-    return hipGetLastError();
+    if (a.T == 0) return hipSuccess;
+    return launch_kernel(ep_dedup_map_kernel, dim3((a.T + NT - 1) / NT), dim3(NT), stream, a);
 }
 
 hipError_t launch_ep_dedup_finish(const EpDedupArgs &a, hipStream_t stream)
 {
     const int n = a.T * a.top_k;
-    if (n > 0) {
-        const int blocks = (n + NT - 1) / NT < 4096 ? (n + NT - 1) / NT : 4096;
-        hipLaunchKernelGGL(ep_dedup_finish_kernel, dim3(blocks), dim3(NT), 0, stream, a);
-    }
-    return hipGetLastError();
+    if (n == 0) return hipSuccess;
+    const int blocks = (n + NT - 1) / NT < 4096 ? (n + NT - 1) / NT : 4096;
+    return launch_kernel(ep_dedup_finish_kernel, dim3(blocks), dim3(NT), stream, a);
 }
 
 }  // namespace siggate

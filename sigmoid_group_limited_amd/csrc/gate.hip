@@ -623,6 +623,25 @@ __device__ __forceinline__ void load_row(const float *p, float (&v)[V])
     }
 }
 
+// A token's summed logits: written out, or through the selection.
+template <int V, int MODE>
+__device__ __forceinline__ void finish_reduce(const GateArgs &a, const float (&lg)[V],
+                                              const int lane, const int t, float *scratch)
+{
+    constexpr int E = V * 64;
+    if constexpr (MODE == MODE_LOGITS) {
+#pragma unroll
+        for (int j = 0; j < V; ++j) a.logits[(size_t)t * E + lane * V + j] = lg[j];
+    } else {
+        float bias_r[V];
+#pragma unroll
+        for (int j = 0; j < V; ++j) bias_r[j] = a.bias ? a.bias[lane * V + j] : 0.0f;
+        select_token<V>(lg, bias_r, lane, a, t, scratch);
+    }
+}
+
+constexpr int ONE_WAVE_SLICES = 16;
+
 // Adds the n_split partial logits of one token in a fixed order -- wave w
 // of NWR sums its contiguous run of slices in ascending order, then wave 0
 // adds the runs in wave order -- and writes the logits or runs the
@@ -645,6 +664,23 @@ __global__ __launch_bounds__(64 * NWR) void gate_reduce_kernel(GateArgs a)
     float lg[V];
 #pragma unroll
     for (int j = 0; j < V; ++j) lg[j] = 0.0f;
+    if constexpr (NWR == 1) {
+        // one wave, at most ONE_WAVE_SLICES slices: every load is issued
+        // before the first add (slices past n_split re-read the last one and
+        // are not added)
+        float q[ONE_WAVE_SLICES][V];
+#pragma unroll
+        for (int u = 0; u < ONE_WAVE_SLICES; ++u)
+            load_row<V>(p + (size_t)min(u, a.n_split - 1) * slice, q[u]);
+#pragma unroll
+        for (int u = 0; u < ONE_WAVE_SLICES; ++u)
+            if (u < a.n_split) {
+#pragma unroll
+                for (int j = 0; j < V; ++j) lg[j] += q[u][j];
+            }
+        finish_reduce<V, MODE>(a, lg, lane, t, scratch);
+        return;
+    }
     int s = s0;
     for (; s + U <= s1; s += U) {
         float q[U][V];
@@ -669,57 +705,37 @@ __global__ __launch_bounds__(64 * NWR) void gate_reduce_kernel(GateArgs a)
     for (int w = 1; w < NWR; ++w)
 #pragma unroll
         for (int j = 0; j < V; ++j) lg[j] += part[w][lane * V + j];
-    if constexpr (MODE == MODE_LOGITS) {
-#pragma unroll
-        for (int j = 0; j < V; ++j) a.logits[(size_t)t * E + lane * V + j] = lg[j];
-    } else {
-        float bias_r[V];
-#pragma unroll
-        for (int j = 0; j < V; ++j) bias_r[j] = a.bias ? a.bias[lane * V + j] : 0.0f;
-        select_token<V>(lg, bias_r, lane, a, t, scratch);
-    }
+    finish_reduce<V, MODE>(a, lg, lane, t, scratch);
 }
 
 template <int E>
 hipError_t launch_for_e(const GateArgs &a, const GatePlan &p, GateMode final_mode,
                         hipStream_t stream)
 {
+    const bool sel = final_mode == MODE_SELECT;
     if (!p.split) {
-        const dim3 grid(p.grid);
-        const dim3 block(64 * 8);
         // 64 tokens: 8 waves, two per SIMD; 32 tokens: 8 waves, the two of a
         // pair split every chunk's k
-        if (p.m_blocks == 2) {
-            if (final_mode == MODE_SELECT)
-                hipLaunchKernelGGL((gate_gemm_kernel<E, 2, 8, MODE_SELECT, 2>), grid, block, 0, stream, a);
-            else
-                hipLaunchKernelGGL((gate_gemm_kernel<E, 2, 8, MODE_LOGITS, 2>), grid, block, 0, stream, a);
-        } else {
-            if (final_mode == MODE_SELECT)
-                hipLaunchKernelGGL((gate_gemm_kernel<E, 1, 8, MODE_SELECT, 2>), grid, block, 0, stream, a);
-            else
-                hipLaunchKernelGGL((gate_gemm_kernel<E, 1, 8, MODE_LOGITS, 2>), grid, block, 0, stream, a);
-        }
-    } else {
-        // split GEMM: 32 tokens x 128 experts, 8 waves (two per SIMD): 4
-        // columns of 32 experts x 2 k-halves of every chunk
         const dim3 grid(p.grid), block(64 * 8);
-        hipLaunchKernelGGL((gate_gemm_kernel<128, 1, 8, MODE_PARTIAL, SPLIT_STAGES>), grid, block, 0, stream, a);
-        // many slices: 16 waves per token, so that each loads few of them
-        const dim3 rgrid(a.T);
-        if (p.n_split > 16) {
-            if (final_mode == MODE_SELECT)
-                hipLaunchKernelGGL((gate_reduce_kernel<E, MODE_SELECT, 16>), rgrid, dim3(1024), 0, stream, a);
-            else
-                hipLaunchKernelGGL((gate_reduce_kernel<E, MODE_LOGITS, 16>), rgrid, dim3(1024), 0, stream, a);
-        } else {
-            if (final_mode == MODE_SELECT)
-                hipLaunchKernelGGL((gate_reduce_kernel<E, MODE_SELECT, 4>), rgrid, dim3(256), 0, stream, a);
-            else
-                hipLaunchKernelGGL((gate_reduce_kernel<E, MODE_LOGITS, 4>), rgrid, dim3(256), 0, stream, a);
-        }
+        if (p.m_blocks == 2)
+            return sel ? launch_kernel(gate_gemm_kernel<E, 2, 8, MODE_SELECT, 2>, grid, block, stream, a)
+                       : launch_kernel(gate_gemm_kernel<E, 2, 8, MODE_LOGITS, 2>, grid, block, stream, a);
+        return sel ? launch_kernel(gate_gemm_kernel<E, 1, 8, MODE_SELECT, 2>, grid, block, stream, a)
+                   : launch_kernel(gate_gemm_kernel<E, 1, 8, MODE_LOGITS, 2>, grid, block, stream, a);
     }
-    return hipGetLastError();
+    // split GEMM: 32 tokens x 128 experts, 8 waves (two per SIMD): 4 columns
+    // of 32 experts x 2 k-halves of every chunk
+    hipError_t e = launch_kernel(gate_gemm_kernel<128, 1, 8, MODE_PARTIAL, SPLIT_STAGES>,
+                                 dim3(p.grid), dim3(64 * 8), stream, a);
+    if (e != hipSuccess) return e;
+    // few slices: one wave per token loads them all at once; more: 16 waves
+    // per token, each loading a contiguous run of them
+    const dim3 rgrid(a.T);
+    if (p.n_split <= ONE_WAVE_SLICES)
+        return sel ? launch_kernel(gate_reduce_kernel<E, MODE_SELECT, 1>, rgrid, dim3(64), stream, a)
+                   : launch_kernel(gate_reduce_kernel<E, MODE_LOGITS, 1>, rgrid, dim3(64), stream, a);
+    return sel ? launch_kernel(gate_reduce_kernel<E, MODE_SELECT, 16>, rgrid, dim3(1024), stream, a)
+               : launch_kernel(gate_reduce_kernel<E, MODE_LOGITS, 16>, rgrid, dim3(1024), stream, a);
 }
 
 }  // namespace

@@ -8,6 +8,19 @@
 
 namespace siggate {
 
+// Launches `kernel` and returns the status of this launch: hipLaunchKernel's
+// own result.  The thread's last-error state is neither read nor cleared, so
+// an error left there by unrelated earlier calls (the caller's, or another
+// library's) is not reported as ours, and stays for its owner to see.
+template <typename T> struct arg_of { typedef T type; };
+template <typename... P>
+inline hipError_t launch_kernel(void (*kernel)(P...), dim3 grid, dim3 block, hipStream_t stream,
+                                typename arg_of<P>::type... args)
+{
+    void *argv[] = {(void *)&args..., nullptr};
+    return hipLaunchKernel((const void *)kernel, grid, block, argv, 0, stream);
+}
+
 // k-elements of x and W staged in LDS per main-loop step
 constexpr int KC = 32;
 // tokens per dispatch block (4 waves of 64 lanes, one token per lane)

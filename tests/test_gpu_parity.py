@@ -289,3 +289,27 @@ def test_empty_batch():
     b = torch.zeros(256, device="cuda")
     w, i = sg.siggate_forward(x, W, b, cfg)
     assert w.shape == (0, 8) and i.shape == (0, 8)
+
+
+def test_stale_hip_error_is_not_ours(o):
+    """An error left in the thread's HIP last-error state by an unrelated
+    call (here a host-side hipSetDevice on a device that does not exist)
+    does not make library calls fail, and is left in place for its owner."""
+    import ctypes
+    hip = ctypes.CDLL("libamdhip64.so")
+    hip.hipGetLastError()
+    assert hip.hipSetDevice(1 << 20) != 0
+    if hip.hipPeekAtLastError() == 0:
+        pytest.skip("this HIP runtime records no last error for hipSetDevice")
+    gc = wl.KIMI_K2
+    gi = wl.make_gate_inputs(256, 7168, gc, seed=12)
+    cfg = cfg_of(gc, 256, 7168)
+    x, W, b = dev_inputs(gi)
+    w, i = sg.siggate_forward(x, W, b, cfg)          # split GEMM + reduction
+    out = sg.siggate_dispatch(x, i, cfg)             # one-launch small dispatch
+    sg.siggate_combine(out.permuted_x, w, out.dest, cfg)
+    torch.cuda.synchronize()
+    ref = oracle_gate(o, gi, cfg)
+    compare_gate(w.cpu().numpy(), i.cpu().numpy(), ref, gc.route_scale)
+    assert hip.hipGetLastError() != 0, "the planted error was consumed"
+    assert hip.hipGetLastError() == 0
