@@ -14,6 +14,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIBRARY = os.path.join(PKG, "libsiggate.so")
+EXAMPLE_SOURCE = os.path.join(PKG, "examples", "route_c.cpp")
+EXAMPLE = os.path.join(PKG, "route_c")
 SOURCES = ["gate.hip", "dispatch.hip", "combine.hip", "ep.hip", "api.hip"]
 ARCH = "gfx950"
 
@@ -45,7 +47,23 @@ def build(verbose: bool = False) -> str:
     if verbose and msgs:
         print("\n".join(msgs))
     os.replace(tmp, LIBRARY)
+    build_example(verbose)
     return LIBRARY
+
+
+def build_example(verbose: bool = False) -> str:
+    """Compile the C ABI example (host code only) against the library."""
+    flags = [f for f in HIPCC_FLAGS if f not in ("-fPIC", "-shared")]
+    cmd = [hipcc(), *flags, "-I", INCLUDE, EXAMPLE_SOURCE, "-L", PKG, "-lsiggate",
+           "-Wl,-rpath,$ORIGIN", "-o", EXAMPLE]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    noise = "is not a recognized feature for this target"
+    msgs = [ln for ln in (res.stdout + res.stderr).splitlines() if noise not in ln]
+    if res.returncode != 0:
+        raise RuntimeError("hipcc failed on the example:\n" + "\n".join(msgs))
+    return EXAMPLE
 
 
 if __name__ == "__main__":
