@@ -65,6 +65,10 @@ SMALL = [
     ("kimi_fused64_T16389_d256", wl.KIMI_K2, 16389, 256),
     ("dsv3_fused64_T16447_d200", wl.DSV3, 16447, 200),
     ("e128_g4_fused64_T16400_d96", wl.GateConfig(128, 4, 2, 6, 1.0), 16400, 96),
+    # degenerate: the kept groups hold exactly top_k experts (all of them win)
+    ("e128_g64_kg4_k8_all_kept_T300_d512", wl.GateConfig(128, 64, 4, 8, 1.0), 300, 512),
+    # every group kept (the group stage selects nothing away)
+    ("e256_g8_kg8_T200_d1024", wl.GateConfig(256, 8, 8, 8, 2.5), 200, 1024),
     ("e128_g1_fused32_T9000_d136", wl.GateConfig(128, 1, 1, 8, 2.5), 9000, 136),
 ]
 
