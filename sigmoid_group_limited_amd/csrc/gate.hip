@@ -169,12 +169,34 @@ __device__ __forceinline__ void select_token(const float (&lg)[V], const float (
 #pragma unroll
     for (int j = 0; j < V; ++j) key[j] = orderable(v[j] + 0.0f);   // -0 -> +0
 
+    // Bracket the K-th largest key X: X <= the wave maximum hi, and, when at
+    // least K lanes hold a key above -inf, X >= the K-th largest of those
+    // lanes' maxima >= the smallest of them, lo.  X then shares every bit
+    // above the first one where hi and lo differ, so the search below
+    // starts there with those bits set.
+    uint32_t lm = key[0];
+#pragma unroll
+    for (int j = 1; j < V; ++j) lm = max(lm, key[j]);
+    const uint32_t none = orderable(-INFINITY);
+    uint32_t hi = lm, lo = lm > none ? lm : 0xffffffffu;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        hi = max(hi, (uint32_t)__shfl_xor((int)hi, off));
+        lo = min(lo, (uint32_t)__shfl_xor((int)lo, off));
+    }
+    uint32_t kth = 0;
+    int b_top = 31;
+    if (__popcll(__ballot(lm > none)) >= K) {
+        const uint32_t diff = hi ^ lo;
+        b_top = diff ? 31 - __clz(diff) : -1;
+        kth = b_top < 0 ? hi : hi & ~(0xffffffffu >> (31 - b_top));
+    }
+
     // K-th largest key, most significant bit first.  Once exactly K keys
     // are >= the prefix found so far, those K are the winners and the lower
     // bits cannot change the choice: stop there (the counts are ballots, so
     // every lane takes the same branch).
-    uint32_t kth = 0;
-    for (int b = 31; b >= 0; --b) {
+    for (int b = b_top; b >= 0; --b) {
         const uint32_t cand = kth | (1u << b);
         int cnt = 0;
 #pragma unroll
