@@ -27,6 +27,10 @@ time per call without host launch cost; the replayed outputs are checked
 against an eager call.  Their gate roofline is the larger of the fp32 MFMA
 and the HBM time (MFMA binds at both sizes).
 
+``secondary.variants`` times the gate alone on the DeepSeek-V3 batch with
+each option of the configuration: softmax scoring, no bias (group maximum),
+and the 0.0 fill with the 1e-20 denominator epsilon, beside the default.
+
 ``overlap`` runs independent batches of the workload with the gates on one
 HIP stream and the dispatches on another (two batches in flight), so that
 one batch's HBM-bound dispatch overlaps the next batch's MFMA-bound gate; it
@@ -187,6 +191,34 @@ class Case:
                 "combine_algorithmic_GBps": comb_bytes / (comb_ms * 1e-3) / 1e9,
                 "combine_hbm_frac": comb_bytes / (comb_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
                 "ep8_metadata_ms": ev[1].elapsed_time(ev[2]) / steps}
+
+    def run_variants(self, steps: int, warmup: int):
+        """Gate-only time of the gate's variants on this workload's inputs:
+        softmax scoring, no bias (group maximum), and the 0.0 fill with the
+        1e-20 denominator epsilon.  Median of ``steps`` HIP-event timings."""
+        import dataclasses
+
+        import torch
+        sg = self.sg
+        out = {}
+        for name, opts, bias in (("sigmoid_default", {}, self.b),
+                                 ("softmax", {"score_func": 1}, self.b),
+                                 ("no_bias", {}, None),
+                                 ("zero_fill_eps", {"mask_zero": 1, "denom_eps": 1e-20}, self.b)):
+            cfg = dataclasses.replace(self.cfg, **opts)
+            call = (lambda cfg=cfg, bias=bias:
+                    sg.siggate_forward(self.x, self.W, bias, cfg, self.weights, self.indices, self.ws))
+            for _ in range(warmup):
+                call()
+            ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+            torch.cuda.synchronize()
+            for e in ev:
+                e[0].record()
+                call()
+                e[1].record()
+            torch.cuda.synchronize()
+            out[name + "_gate_ms"] = float(np.median([e[0].elapsed_time(e[1]) for e in ev]))
+        return out
 
     def algorithmic(self):
         T, d, E, K = self.w.T, self.w.d, self.cfg.E, self.cfg.top_k
@@ -427,6 +459,7 @@ def main():
             "gate_tflops": f2 / (g2 * 1e-3) / 1e12,
             "gate_mfma_frac": f2 / (g2 * 1e-3) / 1e12 / PEAK_FP32_MFMA_TFLOPS,
             "dispatch_algorithmic_GBps": db2 / (d2 * 1e-3) / 1e9,
+            "variants": sec.run_variants(max(5, args.steps // 2), 2),
         }
         del sec
     if not args.no_overlap:
