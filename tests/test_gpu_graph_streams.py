@@ -1,0 +1,114 @@
+"""The library's calls under HIP graph capture and on concurrent streams.
+Needs an MI355X.
+
+The library launches kernels only (no memsets, no allocation), so a whole
+route -- gate, dispatch, combine -- can be captured in one graph.  Each
+replay here follows eager work that rewrites the input, and every replay is
+checked against eager calls on the same input."""
+import numpy as np
+import pytest
+
+import sigmoid_group_limited_amd as sg
+from sigmoid_group_limited_amd import workloads as wl
+from parity import say
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    sg.load_library()
+    yield
+    torch.cuda.synchronize()
+
+
+def _route(x, W, b, cfg, bufs):
+    w, i, ws, out, y = bufs
+    sg.siggate_forward(x, W, b, cfg, w, i, ws)
+    sg.siggate_dispatch(x, i, cfg, out, ws)
+    sg.siggate_combine(out.permuted_x, w, out.dest, cfg, y)
+
+
+def _bufs(cfg):
+    T, K, E, d = cfg.T, cfg.top_k, cfg.E, cfg.d
+    dev = "cuda"
+    out = sg.DispatchOut(torch.empty(E, dtype=torch.int32, device=dev),
+                         torch.empty(E + 1, dtype=torch.int32, device=dev),
+                         torch.empty(T * K, dtype=torch.int32, device=dev),
+                         torch.empty(T * K, dtype=torch.int32, device=dev),
+                         torch.empty((T * K, d), dtype=torch.bfloat16, device=dev))
+    return (torch.empty((T, K), dtype=torch.float32, device=dev),
+            torch.empty((T, K), dtype=torch.int32, device=dev),
+            sg.workspace(cfg, dev), out, torch.empty((T, d), dtype=torch.bfloat16, device=dev))
+
+
+def _snapshot(bufs):
+    w, i, _, out, y = bufs
+    return [t.clone() for t in (w, i, out.tokens_per_expert, out.offsets, out.perm, out.dest,
+                                out.permuted_x, y)]
+
+
+@pytest.mark.parametrize("gc,T,d", [(wl.KIMI_K2, 256, 7168), (wl.DSV3, 64, 7168),
+                                    (wl.DSV3, 2048, 1024), (wl.KIMI_K2, 16384, 512)],
+                         ids=["kimi_T256", "dsv3_T64", "dsv3_T2048", "kimi_T16384"])
+def test_graph_replay_matches_eager(gc, T, d):
+    say(f"[graph] E={gc.n_experts} T={T} d={d}")
+    cfg = sg.Cfg(T, d, gc.n_experts, gc.n_group, gc.topk_group, gc.top_k, gc.route_scale)
+    inputs = [wl.make_gate_inputs(T, d, gc, seed=s) for s in (21, 22, 23)]
+    x = torch.empty((T, d), dtype=torch.bfloat16, device="cuda")
+    W = torch.from_numpy(inputs[0].W).cuda()
+    b = torch.from_numpy(inputs[0].bias).cuda()
+    graph_bufs, eager_bufs = _bufs(cfg), _bufs(cfg)
+    x.copy_(torch.from_numpy(inputs[0].x.view(np.int16)).cuda().view(torch.bfloat16))
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        _route(x, W, b, cfg, graph_bufs)          # warm-up outside the capture
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            _route(x, W, b, cfg, graph_bufs)
+    torch.cuda.synchronize()
+    for rep, gi in enumerate(inputs * 2):
+        # eager work between replays: a new input, then the reference route
+        x.copy_(torch.from_numpy(gi.x.view(np.int16)).cuda().view(torch.bfloat16))
+        _route(x, W, b, cfg, eager_bufs)
+        torch.cuda.synchronize()
+        want = _snapshot(eager_bufs)
+        g.replay()
+        torch.cuda.synchronize()
+        got = _snapshot(graph_bufs)
+        for k, (a, c) in enumerate(zip(got, want)):
+            assert torch.equal(a, c), f"replay {rep}: output {k} differs from the eager call"
+
+
+def test_concurrent_streams_match_sequential():
+    """Independent batches on two streams at once, each with its own
+    workspace and outputs, give exactly the sequential results."""
+    gc = wl.DSV3
+    cfgs = [sg.Cfg(T, 7168, gc.n_experts, gc.n_group, gc.topk_group, gc.top_k, gc.route_scale)
+            for T in (16384, 256)]
+    gis = [wl.make_gate_inputs(c.T, 7168, gc, seed=31 + k) for k, c in enumerate(cfgs)]
+    xs = [torch.from_numpy(g.x.view(np.int16)).cuda().view(torch.bfloat16) for g in gis]
+    W = torch.from_numpy(gis[0].W).cuda()
+    b = torch.from_numpy(gis[0].bias).cuda()
+    seq = []
+    for x, c in zip(xs, cfgs):
+        bufs = _bufs(c)
+        _route(x, W, b, c, bufs)
+        torch.cuda.synchronize()
+        seq.append(_snapshot(bufs))
+    par_bufs = [_bufs(c) for c in cfgs]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    torch.cuda.synchronize()
+    for _ in range(3):
+        for s, x, c, bufs in zip(streams, xs, cfgs, par_bufs):
+            with torch.cuda.stream(s):
+                _route(x, W, b, c, bufs)
+    torch.cuda.synchronize()
+    for want, bufs in zip(seq, par_bufs):
+        for k, (a, c) in enumerate(zip(_snapshot(bufs), want)):
+            assert torch.equal(a, c), f"output {k} differs from the sequential run"
