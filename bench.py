@@ -37,7 +37,9 @@ one batch's HBM-bound dispatch overlaps the next batch's MFMA-bound gate; it
 reports tokens/s over the batches and is not part of ``value``.
 
 ``cpu_baseline`` times the CPU oracle (float64, all host threads) on a
-bounded sample of the same workload.
+bounded sample of the same workload, and reports how the GPU's result on
+those tokens compares with it (``gpu_parity``: tokens exempt for a score
+margin below 1e-6, non-exempt index mismatches, largest weight error).
 """
 from __future__ import annotations
 
@@ -346,7 +348,7 @@ def cpu_baseline(case: Case, budget_s: float = 12.0):
         dr = o.dispatch(r.indices, c.E)
         o.gather_rows(gi.x[:n], dr.perm, c.top_k)
         t2 = time.perf_counter()
-        split["gate"], split["dispatch"] = t1 - t0, t2 - t1
+        split["gate"], split["dispatch"], split["result"] = t1 - t0, t2 - t1, r
         return t2 - t0
 
     n = 256
@@ -360,9 +362,22 @@ def cpu_baseline(case: Case, budget_s: float = 12.0):
         if n_final != n:
             n = n_final
             dt = one(n)
+    # the same tokens on the GPU (the last timed step's outputs) against the
+    # oracle run just timed, with the exemption rule of the parity tests
+    r = split["result"]
+    idx = case.indices[:n].cpu().numpy()
+    wts = case.weights[:n].cpu().numpy().astype(np.float64)
+    exempt = np.minimum(r.margins[:, 0], r.margins[:, 1]) < 1e-6
+    same = np.all(idx == r.indices, axis=1)
+    rel = np.abs(wts[same] - r.weights[same]) / np.maximum(np.abs(r.weights[same]), 1e-30)
+    parity = {"tokens": n, "exempt": int(exempt.sum()),
+              "exempt_matched": int((exempt & same).sum()),
+              "index_mismatch_nonexempt": int((~same & ~exempt).sum()),
+              "weight_max_rel": float(rel.max()) if rel.size else 0.0}
     return dict(value=n / dt, unit="tokens/s", cores=o.num_threads(), kind="oracle",
                 gate_tokens_per_s=n / split["gate"],
                 dispatch_tokens_per_s=n / split["dispatch"],
+                gpu_parity=parity,
                 sample=f"first {n} of {case.w.T} tokens of {case.w.name}: float64 gate, "
                        f"dispatch and row gather of their {n * c.top_k} pairs; {dt:.2f} s")
 
@@ -437,6 +452,7 @@ def main():
             "gate_tflops": achieved,
             "dispatch_algorithmic_GBps": disp_bytes / (disp_ms * 1e-3) / 1e9,
             "dispatch_hbm_frac": disp_bytes / (disp_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+            "pairs_per_s": T * case.cfg.top_k / (ms * 1e-3),
             "roofline_tokens_per_s": T / (flops / (PEAK_FP32_MFMA_TFLOPS * 1e12)
                                           + disp_bytes / (PEAK_HBM_GBS * 1e9)),
         },

@@ -20,7 +20,8 @@ CHILD = textwrap.dedent("""
     import oracle
     from sigmoid_group_limited_amd import workloads as wl
     o = oracle.Oracle(LIB)
-    for gc, T, d in [(wl.DSV3, 37, 64), (wl.KIMI_K2, 20, 40), (wl.GateConfig(128, 64, 4, 8, 1.0), 9, 24)]:
+    for gc, T, d in [(wl.DSV3, 37, 64), (wl.KIMI_K2, 20, 40), (wl.GateConfig(128, 64, 4, 8, 1.0), 9, 24),
+                     (wl.DSV3, 1, 8)]:
         gi = wl.make_gate_inputs(T, d, gc, seed=T)
         for opts in ({}, {"score_func": 1}, {"mask_zero": 1, "denom_eps": 1e-20}, {"renorm": 2}):
             for bias in (gi.bias, None):
@@ -36,6 +37,7 @@ CHILD = textwrap.dedent("""
             if gc.n_experts % ranks == 0:
                 o.ep_send_splits(dr.counts, ranks)
                 o.ep_dedup(r.indices, gc.n_experts, ranks)
+                o.ep_regroup(np.asarray(dr.counts).reshape(ranks, -1))
     o.dispatch(np.zeros((0, 8), np.int32), 256)
     print("sanitized oracle ok")
 """)
