@@ -43,7 +43,8 @@
  *   1 <= top_k <= 8; d a positive multiple of 8; 0 <= T <= 2^31 / top_k.
  * Invalid configurations return SIGGATE_EINVAL: topk_group outside
  * [1, n_group], top_k > topk_group * E / n_group, order not 0 or 1,
- * score_func, renorm or mask_zero out of range, denom_eps negative or NaN.
+ * score_func, renorm, mask_zero or logits_path out of range, denom_eps
+ * negative or NaN.
  */
 #ifndef SIGGATE_H
 #define SIGGATE_H
@@ -76,6 +77,15 @@ typedef struct siggate_cfg {
     int32_t renorm;      /* 0 = renormalise iff sigmoid, 1 = always, 2 = never */
     int32_t mask_zero;   /* 0 = dropped groups -> -inf, 1 = -> 0.0             */
     float denom_eps;     /* added to the renormalisation denominator (>= 0)   */
+    /* How the float32 logits are computed (both give float32 logits of the
+     * same sum; the selection and everything after it are shared):
+     *   0 = on the float32 matrix cores (v_mfma_f32_32x32x2_f32);
+     *   1 = each float32 weight split exactly into three bfloat16 parts
+     *       (W = hi + mid + lo), x * each part (exact products) added into
+     *       float32 accumulators on the bfloat16 matrix cores
+     *       (v_mfma_f32_16x16x32_bf16).  Exact split for |W| >= 2^-110;
+     *       the logits differ from route 0 by float32 summation order only. */
+    int32_t logits_path;
 } siggate_cfg_t;
 
 typedef enum siggate_status {

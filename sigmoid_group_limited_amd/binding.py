@@ -40,7 +40,7 @@ class siggate_cfg_t(ctypes.Structure):
                 ("top_k", ctypes.c_int32), ("route_scale", ctypes.c_float),
                 ("order", ctypes.c_int32), ("score_func", ctypes.c_int32),
                 ("renorm", ctypes.c_int32), ("mask_zero", ctypes.c_int32),
-                ("denom_eps", ctypes.c_float)]
+                ("denom_eps", ctypes.c_float), ("logits_path", ctypes.c_int32)]
 
 
 @dataclass(frozen=True)
@@ -58,11 +58,12 @@ class Cfg:
     renorm: int = 0          # 0 iff sigmoid, 1 always, 2 never
     mask_zero: int = 0       # dropped groups: 0 -> -inf, 1 -> 0.0
     denom_eps: float = 0.0   # added to the renormalisation denominator
+    logits_path: int = 0     # 0 float32 MFMA, 1 exact bfloat16 three-way split
 
     def c(self) -> siggate_cfg_t:
         return siggate_cfg_t(self.T, self.d, self.E, self.n_group, self.topk_group,
                              self.top_k, self.route_scale, self.order, self.score_func,
-                             self.renorm, self.mask_zero, self.denom_eps)
+                             self.renorm, self.mask_zero, self.denom_eps, self.logits_path)
 
     def with_T(self, T: int) -> "Cfg":
         return dataclasses.replace(self, T=T)

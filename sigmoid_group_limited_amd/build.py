@@ -16,7 +16,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIBRARY = os.path.join(PKG, "libsiggate.so")
 EXAMPLE_SOURCE = os.path.join(PKG, "examples", "route_c.cpp")
 EXAMPLE = os.path.join(PKG, "route_c")
-SOURCES = ["gate.hip", "dispatch.hip", "combine.hip", "ep.hip", "api.hip"]
+SOURCES = ["gate.hip", "logits_x3.hip", "dispatch.hip", "combine.hip", "ep.hip", "api.hip"]
 ARCH = "gfx950"
 
 # Packed fp32 arithmetic is switched off for all device code.

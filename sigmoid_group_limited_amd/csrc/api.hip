@@ -29,6 +29,7 @@ siggate_status_t check_gate_cfg(const siggate_cfg_t *c)
     if (c->renorm < 0 || c->renorm > 2) return SIGGATE_EINVAL;
     if (c->mask_zero != 0 && c->mask_zero != 1) return SIGGATE_EINVAL;
     if (!(c->denom_eps >= 0.0f)) return SIGGATE_EINVAL;               // negative or NaN
+    if (c->logits_path != PATH_FP32 && c->logits_path != PATH_BF16X3) return SIGGATE_EINVAL;
     if (c->E != 128 && c->E != 256 && c->E != 384) return SIGGATE_EUNSUPPORTED;
     if (c->n_group > 64 || (c->n_group & (c->n_group - 1)) != 0) return SIGGATE_EUNSUPPORTED;
     if (c->top_k > MAX_TOPK) return SIGGATE_EUNSUPPORTED;
@@ -49,7 +50,7 @@ siggate_status_t check_dispatch_cfg(const siggate_cfg_t *c)
 
 size_t forward_bytes(const siggate_cfg_t *c)
 {
-    return align256(plan_gate(c->T, c->d, c->E).partial_bytes);
+    return align256(plan_gate(c->T, c->d, c->E, c->logits_path).partial_bytes);
 }
 
 GateArgs gate_args(const void *x, const float *W, const float *bias, const siggate_cfg_t *c,
@@ -107,7 +108,7 @@ siggate_status_t siggate_forward(const void *x, const float *W, const float *bia
     if (!aligned16(x) || !aligned16(W) || !aligned16(bias) || !aligned16(weights) ||
         !aligned16(indices) || !aligned16(ws))
         return SIGGATE_EINVAL;
-    const GatePlan p = plan_gate(cfg->T, cfg->d, cfg->E);
+    const GatePlan p = plan_gate(cfg->T, cfg->d, cfg->E, cfg->logits_path);
     if (ws_bytes < align256(p.partial_bytes) || (p.partial_bytes && !ws)) return SIGGATE_EWORKSPACE;
     if (cfg->T == 0) return SIGGATE_OK;
     GateArgs a = gate_args(x, W, bias, cfg, p);
@@ -128,7 +129,7 @@ siggate_status_t siggate_logits(const void *x, const float *W, const siggate_cfg
     if (cfg->T > 0 && (!x || !logits)) return SIGGATE_EINVAL;
     if (!aligned16(x) || !aligned16(W) || !aligned16(logits) || !aligned16(ws))
         return SIGGATE_EINVAL;
-    const GatePlan p = plan_gate(cfg->T, cfg->d, cfg->E);
+    const GatePlan p = plan_gate(cfg->T, cfg->d, cfg->E, cfg->logits_path);
     if (ws_bytes < align256(p.partial_bytes) || (p.partial_bytes && !ws)) return SIGGATE_EWORKSPACE;
     if (cfg->T == 0) return SIGGATE_OK;
     GateArgs a = gate_args(x, W, nullptr, cfg, p);

@@ -687,6 +687,11 @@ __global__ __launch_bounds__(64 * NWR) void gate_reduce_kernel(GateArgs a)
 #pragma unroll
     for (int j = 0; j < V; ++j) lg[j] = 0.0f;
     if constexpr (NWR == 1) {
+        if (a.n_split == 1) {   // a single slice: the logits themselves
+            load_row<V>(p, lg);
+            finish_reduce<V, MODE>(a, lg, lane, t, scratch);
+            return;
+        }
         // one wave, at most ONE_WAVE_SLICES slices: every load is issued
         // before the first add (slices past n_split re-read the last one and
         // are not added)
@@ -746,9 +751,11 @@ hipError_t launch_for_e(const GateArgs &a, const GatePlan &p, GateMode final_mod
                    : launch_kernel(gate_gemm_kernel<E, 1, 8, MODE_LOGITS, 2>, grid, block, stream, a);
     }
     // split GEMM: 32 tokens x 128 experts, 8 waves (two per SIMD): 4 columns
-    // of 32 experts x 2 k-halves of every chunk
-    hipError_t e = launch_kernel(gate_gemm_kernel<128, 1, 8, MODE_PARTIAL, SPLIT_STAGES>,
-                                 dim3(p.grid), dim3(64 * 8), stream, a);
+    // of 32 experts x 2 k-halves of every chunk; or the bfloat16 three-way
+    // route, which writes the same partials
+    hipError_t e = p.x3_bm ? launch_x3_gemm(a, p, stream)
+                           : launch_kernel(gate_gemm_kernel<128, 1, 8, MODE_PARTIAL, SPLIT_STAGES>,
+                                           dim3(p.grid), dim3(64 * 8), stream, a);
     if (e != hipSuccess) return e;
     // few slices: one wave per token loads them all at once; more: 16 waves
     // per token, each loading a contiguous run of them
@@ -772,8 +779,9 @@ constexpr double SPLIT_LATENCY = 4.0;
 constexpr double SPLIT_BYTES_PER_UNIT = 2.25e6;
 constexpr int N_CU = 256;
 
-GatePlan plan_gate(int T, int d, int E)
+GatePlan plan_gate(int T, int d, int E, int path)
 {
+    if (path == PATH_BF16X3) return plan_x3(T, d, E);
     GatePlan p{};
     const int chunks = (d + KC - 1) / KC;
     const long tiles64 = ((long)T + 63) / 64;

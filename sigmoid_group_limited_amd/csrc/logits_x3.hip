@@ -1,0 +1,434 @@
+// logits_x3.hip -- router logits x.W^T on the bfloat16 matrix cores of
+// gfx950, exact to float32 working precision, for the gate of gate.hip.
+//
+// What is computed (DeepSeek-V3.2-Exp · Normalize weights, "Code": Gate
+// forward; Kimi K2 · Normalize weights, the equation for s_{i,t}): the same
+// float32 logits L[t,e] = sum_k x[t,k] * W[e,k] as the float32 GEMM of
+// gate.hip, by another route.
+//
+// The route.  x is bfloat16, so it is exact on the bfloat16 matrix cores.
+// Every float32 weight splits exactly into three bfloat16 parts,
+//   W = hi + mid + lo,
+// hi = W with its low 16 bits cleared (the sign, the exponent and the top 8
+// significant bits), mid the same of the remainder W - hi, and lo = W - hi -
+// mid, which has at most 8 significant bits left and is itself a bfloat16.
+// Each of the three differences is exact (the operands share sign and
+// exponent range), so the split loses nothing for |W| >= 2^-110 (lo stays a
+// normal number).  The products x*hi, x*mid and x*lo are exact in float32
+// (8 x 8 significant bits), and v_mfma_f32_16x16x32_bf16 adds them into
+// float32 accumulators, so L carries float32 accumulation error only, as on
+// the float32 matrix cores, at 16x their per-instruction rate (3 products
+// per term: about 5x the arithmetic rate of the float32 route).
+//
+// Layout of the work.  A workgroup of 4 waves (one per SIMD) owns BM tokens
+// x BN = 64*NBW experts x one slice of the k range, and writes float32
+// partial logits [n_split, T, E]; the reduction of gate.hip adds the slices
+// in a fixed order and runs the selection.  Wave w owns experts
+// [16*NBW*w, 16*NBW*(w+1)) of the tile and all BM tokens, as MB = BM/16
+// token blocks x NBW expert blocks of 16x16 accumulators.  No W element is
+// used by two waves, so each wave loads its W fragments straight from global
+// memory into registers and splits them there (no LDS for W); x, shared by
+// the 4 waves, is staged in LDS as bfloat16 (32 k-columns per chunk,
+// double-buffered).  Global loads run P chunks ahead.  Tiles are ordered as
+// in the split GEMM of gate.hip: token tile fastest, and one contiguous run
+// of tiles per XCD, so the tiles that read one W slice share an L2.
+#include "siggate_internal.h"
+
+namespace siggate {
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+// Two bfloat16 (the upper halves of two float32 bit patterns whose low
+// halves are zero) packed into one word: a in the low half, b in the high.
+__device__ __forceinline__ unsigned pack_hi(unsigned a, unsigned b)
+{
+    return (a >> 16) | (b & 0xffff0000u);
+}
+
+// The exact three-way split of 8 float32 weights (two float4) into three
+// vectors of 8 bfloat16 (hi, mid, lo), element order preserved.
+__device__ __forceinline__ void split3(const f32x4 &w0, const f32x4 &w1, u32x4 &hi, u32x4 &mid,
+                                       u32x4 &lo)
+{
+    unsigned h[8], m[8], l[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const float w = i < 4 ? w0[i] : w1[i - 4];
+        const unsigned hu = __float_as_uint(w) & 0xffff0000u;
+        const float r = w - __uint_as_float(hu);           // exact
+        const unsigned mu = __float_as_uint(r) & 0xffff0000u;
+        const float lw = r - __uint_as_float(mu);          // exact, a bfloat16
+        h[i] = hu;
+        m[i] = mu;
+        l[i] = __float_as_uint(lw);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        hi[j] = pack_hi(h[2 * j], h[2 * j + 1]);
+        mid[j] = pack_hi(m[2 * j], m[2 * j + 1]);
+        lo[j] = pack_hi(l[2 * j], l[2 * j + 1]);
+    }
+}
+
+__device__ __forceinline__ f32x4 mfma_bf16(const u32x4 &a, const u32x4 &b, const f32x4 &c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// The three bfloat16 planes of W (hi, mid, lo) for the pre-split GEMM, in
+// MFMA fragment order: fragment (eb, c) of a plane holds experts
+// 16*eb .. 16*eb+15 and k-columns 32*c .. 32*c+31 as 64 lanes x 8 bfloat16,
+// lane l = expert 16*eb + l%16, k-columns 32*c + 8*(l/16) .. +7 -- the
+// operand layout of v_mfma_f32_16x16x32_bf16 -- so that one wave loads a
+// fragment as 1 KB of consecutive bytes (whole cache lines).  Plane p,
+// fragment (eb, c) starts at element ((p * E/16 + eb) * nc + c) * 512, with
+// nc = ceil(d/32); columns past d are zero.  One thread per lane of a
+// fragment.
+__global__ __launch_bounds__(256) void x3_split_w_kernel(const float *W, uint16_t *planes, int E,
+                                                         int d, int nc)
+{
+    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;   // (eb * nc + c) * 64 + lane
+    const size_t n_lanes = (size_t)(E / 16) * nc * 64;
+    if (i >= n_lanes) return;
+    const int lane = (int)(i & 63);
+    const size_t frag = i >> 6;
+    const int c = (int)(frag % nc);
+    const int eb = (int)(frag / nc);
+    const int k = 32 * c + 8 * (lane >> 4);
+    const float *src = W + (size_t)(16 * eb + (lane & 15)) * d + k;
+    const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
+    const f32x4 w0 = k < d ? __builtin_nontemporal_load((const f32x4 *)src) : z;
+    const f32x4 w1 = k < d ? __builtin_nontemporal_load((const f32x4 *)src + 1) : z;
+    u32x4 h, m, l;
+    split3(w0, w1, h, m, l);
+    u32x4 *const out = (u32x4 *)planes;
+    const size_t plane16 = n_lanes;   // 16-byte units per plane
+    out[i] = h;
+    out[plane16 + i] = m;
+    out[2 * plane16 + i] = l;
+}
+
+// x pieces (16 bytes: 8 k-columns of one token) sit in LDS at row*64 bytes
+// plus a piece slot permuted by the row: rows 4 apart start 16 bytes apart,
+// so the 16 lanes of a fragment read (rows r..r+15, one k-piece) cover all
+// 64 banks once.
+__device__ __forceinline__ int x_slot(int row, int piece) { return row * 4 + (piece ^ ((row >> 2) & 3)); }
+
+// SPLIT: W fragments are loaded as float32 and split in registers (small
+// batches), or loaded as the three planes x3_split_w_kernel wrote (large
+// batches, where the same W slice is split once instead of once per token
+// tile and the matrix cores are not kept waiting on the split).
+template <int BM, int NBW, int P, bool SPLIT>
+__global__ __launch_bounds__(256) void x3_gemm_kernel(GateArgs a)
+{
+    constexpr int MB = BM / 16;              // token blocks per wave
+    constexpr int BN = 64 * NBW;             // experts per workgroup
+    constexpr int XP = BM * KC / 8 / 256;    // 8-element x pieces per thread per chunk
+    static_assert(KC == 32, "one chunk is one MFMA depth (32)");
+    static_assert(BM % 64 == 0 && XP >= 1, "every thread stages whole x pieces");
+    __shared__ __attribute__((aligned(16))) u32x4 xs[SPLIT ? 2 : 3][BM * KC / 8];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    // Workgroup ids go round-robin over the 8 XCDs; each XCD gets one
+    // contiguous run of tile numbers (the grid is a multiple of 8).
+    const int q = (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
+    if (q >= a.n_tiles) return;   // padding of the grid (whole workgroup)
+    const int rq = q / a.t_tiles;
+    const int t0 = (q - rq * a.t_tiles) * BM;
+    const int ks = rq / a.e_tiles;
+    const int e0 = (rq - ks * a.e_tiles) * BN;
+    const int d = a.d;
+    const int c_begin = ks * a.chunks_per_split;
+    const int c_end = min(c_begin + a.chunks_per_split, a.chunks_total);
+
+    // W fragment of expert block n: lane l holds expert
+    // e0 + 16*(NBW*wave + n) + l%16, k-columns k0 + 8*(l/16) .. +7 (the
+    // operand layout of v_mfma_f32_16x16x32_bf16; x uses the same k order).
+    // Pieces past d (d is a multiple of 8) read the last in-range piece
+    // instead; their x is zero, so they add nothing.
+    const int f_row = lane & 15;
+    const int f_k = 8 * (lane >> 4);
+    // float32 W: row offsets; pre-split planes: this lane's 16 bytes in
+    // fragment (expert block, chunk 0) of plane 0, in 16-byte units
+    const int nc = a.chunks_total;
+    const size_t plane16 = (size_t)(a.E / 16) * nc * 64;
+    size_t wrow[NBW];
+#pragma unroll
+    for (int n = 0; n < NBW; ++n) {
+        const int eb = e0 / 16 + NBW * wave + n;
+        wrow[n] = SPLIT ? (size_t)(16 * eb + f_row) * d : (size_t)eb * nc * 64 + lane;
+    }
+    // x piece p = tid + 256*i: token row p/4, k-columns 8*(p%4) .. +7 of the
+    // chunk; rows past T read row T-1 (their logits are dropped).
+    const uint16_t *xrow[XP];
+    int xcol[XP], xdst[XP];
+#pragma unroll
+    for (int i = 0; i < XP; ++i) {
+        const int p = tid + 256 * i;
+        xrow[i] = a.x + (size_t)min(t0 + p / 4, a.T - 1) * d;
+        xcol[i] = 8 * (p % 4);
+        xdst[i] = x_slot(p / 4, p % 4);
+    }
+
+    auto load_x = [&](int c, u32x4 (&x)[XP]) {
+        const int k0 = c * KC;
+#pragma unroll
+        for (int i = 0; i < XP; ++i) x[i] = *(const u32x4 *)(xrow[i] + min(k0 + xcol[i], d - 8));
+    };
+    // Pieces past d are zeroed by a second store, in the last chunk only (a
+    // uniform branch), so that the common store waits on nothing but its own
+    // chunk's loads.
+    auto store_x = [&](int c, int buf, const u32x4 (&x)[XP]) {
+        const int k0 = c * KC;
+#pragma unroll
+        for (int i = 0; i < XP; ++i) xs[buf][xdst[i]] = x[i];
+        if (k0 + KC > d) {
+#pragma unroll
+            for (int i = 0; i < XP; ++i)
+                if (k0 + xcol[i] >= d) xs[buf][xdst[i]] = u32x4{0u, 0u, 0u, 0u};
+        }
+    };
+    auto read_a = [&](int buf, u32x4 (&f)[MB]) {
+#pragma unroll
+        for (int m = 0; m < MB; ++m) f[m] = xs[buf][x_slot(16 * m + f_row, lane >> 4)];
+    };
+
+    f32x4 acc[MB][NBW];
+#pragma unroll
+    for (int m = 0; m < MB; ++m)
+#pragma unroll
+        for (int n = 0; n < NBW; ++n) acc[m][n] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+    constexpr int SG_MFMA = 0x008, SG_VMEM_READ = 0x020, SG_DS_READ = 0x100, SG_DS_WRITE = 0x200;
+    if (c_begin < c_end) {
+        const int c_last = c_end - 1;
+        const int cb = c_begin;
+        const int nch = c_end - c_begin;
+        if constexpr (SPLIT) {
+            // float32 W in P register stages; x double-buffered in LDS.  One
+            // chunk: A fragments from LDS, the split of this chunk's W, the
+            // refill of its stage with chunk c+P, 3*MB*NBW MFMAs, then chunk
+            // c+1's x into the other buffer and the barrier that publishes it.
+            struct Stage {
+                f32x4 w[NBW][2];
+                u32x4 x[XP];
+            };
+            auto load_global = [&](int c, Stage &st) {
+                const int wk = min(c * KC + f_k, d - 8);
+#pragma unroll
+                for (int n = 0; n < NBW; ++n) {
+                    st.w[n][0] = *(const f32x4 *)(a.W + wrow[n] + wk);
+                    st.w[n][1] = *(const f32x4 *)(a.W + wrow[n] + wk + 4);
+                }
+                load_x(c, st.x);
+            };
+            auto step = [&](int c, int buf, Stage &cur, const Stage &next) {
+                u32x4 af[MB];
+                read_a(buf, af);
+                u32x4 bw[3][NBW];
+#pragma unroll
+                for (int n = 0; n < NBW; ++n) split3(cur.w[n][0], cur.w[n][1], bw[0][n], bw[1][n], bw[2][n]);
+                load_global(min(c + P, c_last), cur);
+#pragma unroll
+                for (int pl = 0; pl < 3; ++pl)
+#pragma unroll
+                    for (int n = 0; n < NBW; ++n)
+#pragma unroll
+                        for (int m = 0; m < MB; ++m) acc[m][n] = mfma_bf16(af[m], bw[pl][n], acc[m][n]);
+                store_x(min(c + 1, c_last), buf ^ 1, next.x);
+                __syncthreads();
+            };
+            Stage st[P];
+#pragma unroll
+            for (int j = 0; j < P; ++j) load_global(min(cb + j, c_last), st[j]);
+            store_x(cb, 0, st[0].x);
+            __syncthreads();
+            // local chunk i uses LDS buffer i%2 and stage i%P: unrolled by
+            // lcm(P, 2) so that both stay static
+            constexpr int U = P % 2 ? 2 * P : P;
+            int i = 0;
+            for (; i + U <= nch; i += U) {
+#pragma unroll
+                for (int u = 0; u < U; ++u) step(cb + i + u, u & 1, st[u % P], st[(u + 1) % P]);
+            }
+#pragma unroll
+            for (int u = 0; u < U - 1; ++u)
+                if (i + u < nch) step(cb + i + u, u & 1, st[u % P], st[(u + 1) % P]);
+        } else {
+            // Pre-split planes.  Local chunk i: MFMAs on A fragments af[i%2]
+            // (read during chunk i-1) and W fragments wst[i%2] (each refilled
+            // with chunk i+2 right after its last MFMA, so the loads spread
+            // one per MB MFMAs); meanwhile the A fragments of chunk i+1 come
+            // from LDS buffer (i+1)%3, and x of chunk i+2 (loaded two chunks
+            // earlier) goes to buffer (i+2)%3.  With x three-buffered, no
+            // MFMA waits on an LDS read issued in its own chunk, and the one
+            // barrier per chunk publishes chunk i+2 two chunks ahead.
+            u32x4 wst[2][NBW][3];
+            u32x4 xst[2][XP];
+            u32x4 af[2][MB];
+            const u32x4 *const planes = (const u32x4 *)a.w_planes;
+            auto load_w = [&](int c, u32x4 (&w)[NBW][3]) {
+#pragma unroll
+                for (int n = 0; n < NBW; ++n)
+#pragma unroll
+                    for (int pl = 0; pl < 3; ++pl) w[n][pl] = planes[pl * plane16 + wrow[n] + (size_t)c * 64];
+            };
+            load_w(cb, wst[0]);
+            load_w(min(cb + 1, c_last), wst[1]);
+            load_x(cb, xst[0]);
+            load_x(min(cb + 1, c_last), xst[1]);
+            store_x(cb, 0, xst[0]);
+            store_x(min(cb + 1, c_last), 1, xst[1]);
+            load_x(min(cb + 2, c_last), xst[0]);
+            load_x(min(cb + 3, c_last), xst[1]);
+            __syncthreads();
+            read_a(0, af[0]);
+            auto pstep = [&](int i, int ab, int sb) {   // ab = i % 3, sb = i % 2
+                const int c = cb + i;
+                read_a((ab + 1) % 3, af[sb ^ 1]);
+                const int cw = min(c + 2, c_last);
+#pragma unroll
+                for (int pl = 0; pl < 3; ++pl)
+#pragma unroll
+                    for (int n = 0; n < NBW; ++n) {
+                        const u32x4 b = wst[sb][n][pl];
+#pragma unroll
+                        for (int m = 0; m < MB; ++m) acc[m][n] = mfma_bf16(af[sb][m], b, acc[m][n]);
+                        wst[sb][n][pl] = planes[pl * plane16 + wrow[n] + (size_t)cw * 64];
+                    }
+                __builtin_amdgcn_sched_group_barrier(SG_DS_READ, MB, 0);
+#pragma unroll
+                for (int g = 0; g < 3 * NBW; ++g) {
+                    __builtin_amdgcn_sched_group_barrier(SG_MFMA, MB, 0);
+                    __builtin_amdgcn_sched_group_barrier(SG_VMEM_READ, 1, 0);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                store_x(min(c + 2, c_last), (ab + 2) % 3, xst[sb]);
+                load_x(min(c + 4, c_last), xst[sb]);
+                __syncthreads();
+            };
+            int i = 0;
+            for (; i + 6 <= nch; i += 6) {
+#pragma unroll
+                for (int u = 0; u < 6; ++u) pstep(i + u, u % 3, u & 1);
+            }
+#pragma unroll
+            for (int u = 0; u < 5; ++u)
+                if (i + u < nch) pstep(i + u, u % 3, u & 1);
+        }
+    }
+
+    // Accumulator r of block (m, n) in lane l: token t0 + 16m + 4(l/16) + r,
+    // expert e0 + 16(NBW*wave + n) + l%16.
+    float *const out = a.partial + (size_t)ks * a.T * a.E;
+#pragma unroll
+    for (int m = 0; m < MB; ++m)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int t = t0 + 16 * m + 4 * (lane >> 4) + r;
+            if (t < a.T) {
+#pragma unroll
+                for (int n = 0; n < NBW; ++n)
+                    out[(size_t)t * a.E + e0 + 16 * (NBW * wave + n) + f_row] = acc[m][n][r];
+            }
+        }
+}
+
+// Tile shapes: BM tokens x 64*NBW experts.
+struct X3Shape {
+    int bm, nbw;
+};
+constexpr X3Shape X3_SHAPES[] = {{128, 3}, {128, 2}, {64, 2}, {64, 1}};
+
+// Cost model, in MFMA cycles of one SIMD: a chunk of a BM x 64*NBW tile is
+// 3 * (BM/16) * NBW MFMAs of 16 cycles plus X3_CHUNK_OVERHEAD; a workgroup
+// adds X3_LATENCY; workgroups beyond one per compute unit queue behind it;
+// the partial logits cross HBM twice at X3_BYTES_PER_CYCLE.
+constexpr double X3_CHUNK_OVERHEAD = 150.0;
+constexpr double X3_LATENCY = 3000.0;
+constexpr double X3_BYTES_PER_CYCLE = 2400.0;
+constexpr int X3_N_CU = 256;
+constexpr int X3_STAGES = 3;
+// From this many tokens on, W is split once per call into planes (the split
+// kernel reads W once and writes 1.5x its bytes) instead of in registers by
+// every token tile.
+constexpr int X3_PRESPLIT_MIN_T = 4096;
+
+size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+template <int BM, int NBW>
+hipError_t launch_shape(const GateArgs &a, const GatePlan &p, hipStream_t stream)
+{
+    const dim3 grid(p.grid), block(256);
+    if (p.x3_presplit) return launch_kernel(x3_gemm_kernel<BM, NBW, X3_STAGES, false>, grid, block, stream, a);
+    return launch_kernel(x3_gemm_kernel<BM, NBW, X3_STAGES, true>, grid, block, stream, a);
+}
+
+}  // namespace
+
+GatePlan plan_x3(int T, int d, int E)
+{
+    GatePlan p{};
+    p.split = true;
+    const int chunks = (d + KC - 1) / KC;
+    double best = 1e300;
+    for (const X3Shape &sh : X3_SHAPES) {
+        const int bn = 64 * sh.nbw;
+        if (E % bn != 0) continue;
+        const long tiles = ((long)T + sh.bm - 1) / sh.bm * (E / bn);
+        const double chunk_cost = 3.0 * (sh.bm / 16) * sh.nbw * 16.0 + X3_CHUNK_OVERHEAD;
+        for (int s = 1; s <= chunks; ++s) {
+            const int cps = (chunks + s - 1) / s;
+            if ((chunks + cps - 1) / cps != s) continue;   // s slices of cps chunks
+            const long n = tiles * s;
+            const double rounds = (double)((n + X3_N_CU - 1) / X3_N_CU);
+            const double cost = rounds * (cps * chunk_cost + X3_LATENCY) +
+                                2.0 * s * (double)T * E * sizeof(float) / X3_BYTES_PER_CYCLE;
+            if (cost < best) {
+                best = cost;
+                p.x3_bm = sh.bm;
+                p.x3_nbw = sh.nbw;
+                p.n_split = s;
+                p.chunks_per_split = cps;
+                p.t_tiles = (T + sh.bm - 1) / sh.bm;
+                p.e_tiles = E / bn;
+            }
+        }
+    }
+    const long n = (long)p.t_tiles * p.e_tiles * p.n_split;
+    p.grid = (int)((n + 7) / 8 * 8);
+    p.m_blocks = 0;
+    p.x3_presplit = T >= X3_PRESPLIT_MIN_T;
+    const size_t partials = (size_t)p.n_split * (size_t)T * (size_t)E * sizeof(float);
+    p.planes_offset = p.x3_presplit ? align256(partials) : 0;
+    // planes: 3 x E x (chunks * 32) bfloat16
+    p.partial_bytes = p.x3_presplit ? p.planes_offset + (size_t)3 * E * chunks * KC * sizeof(uint16_t)
+                                    : partials;
+    return p;
+}
+
+hipError_t launch_x3_gemm(const GateArgs &args, const GatePlan &p, hipStream_t stream)
+{
+    GateArgs a = args;
+    if (p.x3_presplit) {
+        uint16_t *planes = (uint16_t *)((char *)a.partial + p.planes_offset);
+        const size_t n_lanes = (size_t)(a.E / 16) * a.chunks_total * 64;
+        const hipError_t e = launch_kernel(x3_split_w_kernel, dim3((unsigned)((n_lanes + 255) / 256)),
+                                           dim3(256), stream, a.W, planes, a.E, a.d, a.chunks_total);
+        if (e != hipSuccess) return e;
+        a.w_planes = planes;
+    }
+    if (p.x3_bm == 128 && p.x3_nbw == 3) return launch_shape<128, 3>(a, p, stream);
+    if (p.x3_bm == 128 && p.x3_nbw == 2) return launch_shape<128, 2>(a, p, stream);
+    if (p.x3_bm == 64 && p.x3_nbw == 2) return launch_shape<64, 2>(a, p, stream);
+    if (p.x3_bm == 64 && p.x3_nbw == 1) return launch_shape<64, 1>(a, p, stream);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace siggate

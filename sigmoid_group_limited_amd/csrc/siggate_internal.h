@@ -50,6 +50,7 @@ struct GateArgs {
     int32_t *indices;       // [T, top_k]      (MODE_SELECT)
     float *logits;          // [T, E]          (MODE_LOGITS)
     float *partial;         // [n_split, T, E] (MODE_PARTIAL, reduce input)
+    const uint16_t *w_planes;   // [3, E, d] bfloat16 parts of W (pre-split x3 route)
 };
 
 // How the logits GEMM is cut for a given T.
@@ -58,17 +59,27 @@ struct GateArgs {
 //   split: one workgroup owns 32 tokens x 128 experts x one k-slice
 //          and writes float32 partial logits [n_split, T, E]; a second kernel
 //          adds the slices and runs the selection.
+//   x3:    the split layout with the bfloat16 three-way route of
+//          logits_x3.hip: x3_bm tokens x 64*x3_nbw experts x one k-slice.
 struct GatePlan {
     bool split;
+    int x3_bm, x3_nbw;      // x3 tile (0, 0 on the float32 route)
+    bool x3_presplit;       // x3: W split once into planes in the workspace
+    size_t planes_offset;   // x3 pre-split: byte offset of the planes
     int m_blocks;           // 32-token blocks per workgroup: 1 or 2 (fused), 1 (split)
     int n_split;            // k-slices (split path)
     int chunks_per_split;
     int t_tiles, e_tiles;   // split path tiles
     int grid;               // workgroups of the GEMM launch
-    size_t partial_bytes;   // workspace for split partials
+    size_t partial_bytes;   // workspace: split partials (+ x3 planes)
 };
 
-GatePlan plan_gate(int T, int d, int E);
+// Logits routes (siggate_cfg_t.logits_path)
+enum LogitsPath { PATH_FP32 = 0, PATH_BF16X3 = 1 };
+
+GatePlan plan_gate(int T, int d, int E, int path);
+GatePlan plan_x3(int T, int d, int E);
+hipError_t launch_x3_gemm(const GateArgs &a, const GatePlan &p, hipStream_t stream);
 
 // Launchers; return hipSuccess or the launch error.
 hipError_t launch_gate(const GateArgs &a, const GatePlan &p, int E, GateMode final_mode,

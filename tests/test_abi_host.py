@@ -2,6 +2,7 @@
 every function include/siggate.h declares, sizes workspaces, and rejects bad
 arguments before anything is enqueued."""
 import ctypes
+import dataclasses
 import os
 import re
 
@@ -55,6 +56,11 @@ def test_workspace_bytes():
     # split-k at small T needs partial logits
     assert sg.siggate_workspace_bytes(KIMI) >= 256 * 384 * 4 * 2
     assert sg.siggate_workspace_bytes(sg.Cfg(0, 7168, 256, 8, 4, 8, 2.5)) == 0
+    # the bfloat16 three-way route always writes partial logits (at least one
+    # slice), for the reduction that runs the selection
+    x3 = dataclasses.replace(big, logits_path=1)
+    assert sg.siggate_workspace_bytes(x3) >= 16384 * 256 * 4
+    assert sg.siggate_workspace_bytes(dataclasses.replace(KIMI, logits_path=1)) >= 256 * 384 * 4
 
 
 def call_forward(cfg, x=FAKE, W=FAKE, bias=FAKE, w=FAKE, i=FAKE, ws=FAKE, ws_bytes=1 << 40):
@@ -74,7 +80,7 @@ def call_dispatch(cfg, x=FAKE, idx=FAKE, tpe=FAKE, off=FAKE, perm=FAKE, dest=FAK
     dict(top_k=33, topk_group=1), dict(order=2), dict(T=-1), dict(d=0),
     dict(route_scale=float("nan")), dict(E=256, n_group=256, topk_group=1, top_k=1),
     dict(score_func=2), dict(renorm=3), dict(renorm=-1), dict(mask_zero=2),
-    dict(denom_eps=-1e-20), dict(denom_eps=float("nan")),
+    dict(denom_eps=-1e-20), dict(denom_eps=float("nan")), dict(logits_path=2), dict(logits_path=-1),
 ])
 def test_forward_rejects_invalid(bad):
     fields = DSV3.__dict__ | bad
@@ -150,8 +156,8 @@ def test_combine_checks():
 
 
 def test_cfg_struct_layout():
-    """The ctypes mirror matches the C struct: 12 four-byte fields."""
-    assert ctypes.sizeof(binding.siggate_cfg_t) == 48
+    """The ctypes mirror matches the C struct: 13 four-byte fields."""
+    assert ctypes.sizeof(binding.siggate_cfg_t) == 52
     names = [f[0] for f in binding.siggate_cfg_t._fields_]
     with open(HEADER) as f:
         text = f.read()
