@@ -36,6 +36,14 @@ HIP stream and the dispatches on another (two batches in flight), so that
 one batch's HBM-bound dispatch overlaps the next batch's MFMA-bound gate; it
 reports tokens/s over the batches and is not part of ``value``.
 
+``bf16x3`` repeats the step, the secondary batch and the decode lines with
+the logits on the bfloat16 three-way route (cfg.logits_path = 1): W split
+exactly into hi + mid + lo bfloat16 parts, every product exact, float32
+accumulation on the bf16 matrix cores.  Same outputs up to float32 summation
+order (``rows_equal_float32_route``); its roofline counts the 3 * 2*T*d*E
+bf16 flops it executes against the bf16 peak.  ``value`` stays the float32
+route's.
+
 ``cpu_baseline`` times the CPU oracle (float64, all host threads) on a
 bounded sample of the same workload, and reports how the GPU's result on
 those tokens compares with it (``gpu_parity``: tokens exempt for a score
@@ -87,7 +95,7 @@ def gate_traffic(workload: str, n_launch_bytes: float):
 class Case:
     """Device-resident inputs, outputs and workspace of one workload."""
 
-    def __init__(self, name: str):
+    def __init__(self, name: str, logits_path: int = 0):
         import torch
 
         import sigmoid_group_limited_amd as sg
@@ -98,7 +106,7 @@ class Case:
         self.gi = wl.workload_inputs(self.w)
         log(f"[bench] {name}: inputs drawn in {time.time() - t0:.1f}s")
         self.cfg = sg.Cfg(self.w.T, self.w.d, c.n_experts, c.n_group, c.topk_group,
-                          c.top_k, c.route_scale)
+                          c.top_k, c.route_scale, logits_path=logits_path)
         dev = "cuda"
         self.x = torch.from_numpy(self.gi.x.view(np.int16)).to(dev).view(torch.bfloat16)
         self.W = torch.from_numpy(self.gi.W).to(dev)
@@ -280,11 +288,39 @@ def overlap_line(name: str, steps: int, warmup: int):
                     "not the step of value"}
 
 
-def decode_line(name: str, calls: int = 20, replays: int = 5):
+PEAK_BF16_MFMA_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
+
+
+def bf16x3_line(name: str, steps: int, warmup: int, ref_indices=None):
+    """The same step with the logits on the bfloat16 three-way route
+    (cfg.logits_path = 1: W split exactly into three bfloat16 parts, three
+    exact products per term accumulated in float32).  Its roofline counts the
+    3 * 2*T*d*E bf16 MFMA flops the route executes against the bf16 peak.
+    ``rows_equal_float32_route`` is the share of tokens whose indices equal
+    those of the float32 route."""
+    case = Case(name, logits_path=1)
+    ms, g, dd = case.run(steps, warmup)
+    T, d, E = case.w.T, case.w.d, case.cfg.E
+    x3_flops = 3 * 2.0 * T * d * E
+    out = {"workload": name, "value": T / (ms * 1e-3), "unit": "tokens/s", "ms_per_step": ms,
+           "gate_ms": g, "dispatch_ms": dd,
+           "gate_ms_median": case.medians[0], "dispatch_ms_median": case.medians[1],
+           "gate_equivalent_fp32_tflops": 2.0 * T * d * E / (g * 1e-3) / 1e12,
+           "roofline": {"bound": "mfma", "achieved": x3_flops / (g * 1e-3) / 1e12,
+                        "peak": PEAK_BF16_MFMA_TFLOPS, "unit": "TFLOP/s",
+                        "frac": x3_flops / (g * 1e-3) / 1e12 / PEAK_BF16_MFMA_TFLOPS,
+                        "note": "whole gate (W split, GEMM, selection) against 3*2*T*d*E bf16 flops"}}
+    if ref_indices is not None:
+        out["rows_equal_float32_route"] = float((case.indices == ref_indices).all(1).float().mean())
+    del case
+    return out
+
+
+def decode_line(name: str, calls: int = 20, replays: int = 5, logits_path: int = 0):
     """Gate and gate+dispatch of one decode-size batch, timed by replaying
     ``calls`` back-to-back calls captured in a HIP graph."""
     import torch
-    case = Case(name)
+    case = Case(name, logits_path)
     case.forward()
     case.dispatch()
     torch.cuda.synchronize()
@@ -316,10 +352,12 @@ def decode_line(name: str, calls: int = 20, replays: int = 5):
             and torch.equal(case.out.permuted_x, ref_x))
     T = case.w.T
     flops, gate_bytes, disp_bytes = case.algorithmic()
-    t_mfma = flops / (PEAK_FP32_MFMA_TFLOPS * 1e12) * 1e6
+    # the bfloat16 three-way route executes 3x the flops on the bf16 peak
+    t_mfma = (flops / (PEAK_FP32_MFMA_TFLOPS * 1e12) if logits_path == 0
+              else 3 * flops / (PEAK_BF16_MFMA_TFLOPS * 1e12)) * 1e6
     t_hbm = gate_bytes / (PEAK_HBM_GBS * 1e9) * 1e6
     t_roof = max(t_mfma, t_hbm)
-    return {"workload": name, "T": T, "E": case.cfg.E,
+    return {"workload": name, "T": T, "E": case.cfg.E, "logits_path": logits_path,
             "gate_us": gate_us, "dispatch_us": path_us - gate_us, "path_us": path_us,
             "gate_tokens_per_s": T / (gate_us * 1e-6), "path_tokens_per_s": T / (path_us * 1e-6),
             "gate_bound": "mfma" if t_mfma >= t_hbm else "hbm",
@@ -395,6 +433,8 @@ def main():
     ap.add_argument("--no-cold", action="store_true", help="skip the scrubbed (cold) steps")
     ap.add_argument("--no-overlap", action="store_true",
                     help="skip the two-stream run of two independent batches")
+    ap.add_argument("--no-bf16x3", action="store_true",
+                    help="skip the lines of the bfloat16 three-way logits route")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (counter calibration)")
     args = ap.parse_args()
@@ -482,6 +522,15 @@ def main():
         result["overlap"] = overlap_line(args.workload, max(8, args.steps), 2)
     if not args.no_decode:
         result["decode"] = [decode_line("kimi-k2-decode"), decode_line("dsv3-tiny")]
+    if not args.no_bf16x3:
+        ref = case.indices.clone()
+        x3 = {"default": bf16x3_line(args.workload, args.steps, args.warmup, ref)}
+        if args.secondary:
+            x3["secondary"] = bf16x3_line(args.secondary, max(5, args.steps // 2), 2)
+        if not args.no_decode:
+            x3["decode"] = [decode_line("kimi-k2-decode", logits_path=1),
+                            decode_line("dsv3-tiny", logits_path=1)]
+        result["bf16x3"] = x3
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(case)
     print(json.dumps(result), flush=True)
