@@ -340,6 +340,190 @@ __global__ __launch_bounds__(256) void x3_gemm_kernel(GateArgs a)
         }
 }
 
+// Large batches: the pre-split planes on 8 waves (two per SIMD -- one wave
+// per SIMD cannot issue these MFMAs back to back at full rate).  The waves
+// are 4 expert quarters (16*NBW experts each) x 2 k-halves: a chunk is 64
+// k-columns and wave (wn, wk) takes its 32-column half wk, so every W
+// fragment is still loaded by exactly one wave.  x is staged in LDS 64
+// columns (128 bytes of a row) at a time, 8 threads per row (whole cache
+// lines), double-buffered.  Each wave holds its W fragments for two chunks
+// in registers and refills each one right after its last MFMA.  At the end
+// the k-half-1 wave of each quarter hands its sums to the k-half-0 wave
+// through LDS, which adds them after its own (a fixed order) and writes the
+// partial logits.  (Each wave's W fragments are refilled with the next chunk
+// in the order they are consumed, so one register buffer gives every load a
+// whole chunk of MFMA work to land in.)
+template <int BM, int NBW>
+struct X3Wide {
+    static constexpr int MB = BM / 16;               // token blocks per wave
+    static constexpr int BN = 64 * NBW;              // experts per workgroup
+    static constexpr int XQ = BM * 64 / 8 / 512;     // x pieces per thread per chunk
+    static constexpr int STAGE = 2 * BM * 8;         // 16-byte slots: two x buffers
+    static constexpr int RED = 4 * MB * NBW * 64;    // 16-byte slots: k-split hand-over
+    static constexpr int SLOTS = STAGE > RED ? STAGE : RED;
+    static_assert(XQ >= 1, "every thread stages whole x pieces");
+};
+
+// 16-byte x pieces of one 128-byte row: 8 per row, permuted by the row so
+// that the 16 lanes of a fragment read (rows r..r+15, one piece) cover all
+// 64 banks once.
+__device__ __forceinline__ int xw_slot(int row, int piece) { return row * 8 + (piece ^ ((row >> 1) & 7)); }
+
+template <int BM, int NBW>
+__global__ __launch_bounds__(512) void x3_gemm8_kernel(GateArgs a)
+{
+    using S = X3Wide<BM, NBW>;
+    constexpr int MB = S::MB, XQ = S::XQ;
+    __shared__ __attribute__((aligned(16))) u32x4 smem[S::SLOTS];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wn = wave & 3;          // expert quarter
+    const int wk = wave >> 2;         // k-half of every chunk
+    const int q = (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
+    if (q >= a.n_tiles) return;       // padding of the grid (whole workgroup)
+    const int rq = q / a.t_tiles;
+    const int t0 = (q - rq * a.t_tiles) * BM;
+    const int ks = rq / a.e_tiles;
+    const int e0 = (rq - ks * a.e_tiles) * S::BN;
+    const int d = a.d;
+    const int nc = a.chunks_total;                       // 32-column fragments per row
+    const int c_begin = ks * a.chunks_per_split;         // in 32-column units
+    const int c_end = min(c_begin + a.chunks_per_split, nc);
+    const int c_last = c_end - 1;
+    const int npairs = (c_end - c_begin + 1) / 2;        // 64-column chunks
+
+    const int f_row = lane & 15;
+    const size_t plane16 = (size_t)(a.E / 16) * nc * 64;
+    const u32x4 *const planes = (const u32x4 *)a.w_planes;
+    size_t wbase[NBW];
+#pragma unroll
+    for (int n = 0; n < NBW; ++n) wbase[n] = (size_t)(e0 / 16 + NBW * wn + n) * nc * 64 + lane;
+    // W fragment (plane pl, block n) of 64-column chunk j: 32-column
+    // fragment c_begin + 2j + wk (clamped; a fragment past the slice or past
+    // d meets zero x)
+    auto wfrag = [&](int j, int n, int pl) {
+        const int c = min(c_begin + 2 * j + wk, c_last);
+        return planes[pl * plane16 + wbase[n] + (size_t)c * 64];
+    };
+    // x piece i of this thread: row tid/8 + 64i, k-piece tid%8 of the chunk
+    const int kp = tid & 7;
+    const uint16_t *xrow[XQ];
+    int xsl[XQ];
+#pragma unroll
+    for (int i = 0; i < XQ; ++i) {
+        const int row = (tid >> 3) + 64 * i;
+        xrow[i] = a.x + (size_t)min(t0 + row, a.T - 1) * d;
+        xsl[i] = xw_slot(row, kp);
+    }
+    auto load_x = [&](int j, u32x4 (&x)[XQ]) {
+        const int k = (c_begin + 2 * j) * KC + 8 * kp;
+#pragma unroll
+        for (int i = 0; i < XQ; ++i) x[i] = *(const u32x4 *)(xrow[i] + min(k, d - 8));
+    };
+    // pieces past d or past the slice are stored as zeros (rare: a second
+    // store in a uniform branch keeps the common path free of selects)
+    auto store_x = [&](int j, int buf, const u32x4 (&x)[XQ]) {
+        u32x4 *const xs = smem + buf * BM * 8;
+#pragma unroll
+        for (int i = 0; i < XQ; ++i) xs[xsl[i]] = x[i];
+        if ((c_begin + 2 * j + 2) * KC > d || c_begin + 2 * j + 2 > c_end) {
+            const int c = c_begin + 2 * j + (kp >> 2);
+            if (c >= c_end || c * KC + 8 * (kp & 3) >= d) {
+#pragma unroll
+                for (int i = 0; i < XQ; ++i) xs[xsl[i]] = u32x4{0u, 0u, 0u, 0u};
+            }
+        }
+    };
+
+    f32x4 acc[MB][NBW];
+#pragma unroll
+    for (int m = 0; m < MB; ++m)
+#pragma unroll
+        for (int n = 0; n < NBW; ++n) acc[m][n] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+    constexpr int SG_MFMA = 0x008, SG_VMEM_READ = 0x020, SG_DS_READ = 0x100;
+    if (npairs > 0) {
+        u32x4 wst[NBW][3];
+        u32x4 xst[XQ];
+#pragma unroll
+        for (int n = 0; n < NBW; ++n)
+#pragma unroll
+            for (int pl = 0; pl < 3; ++pl) wst[n][pl] = wfrag(0, n, pl);
+        load_x(0, xst);
+        store_x(0, 0, xst);
+        load_x(min(1, npairs - 1), xst);
+        __syncthreads();
+        // chunk j: A fragments from buffer j%2, MFMAs on the W fragments
+        // (each refilled with chunk j+1 after its last use), chunk j+1's x
+        // into the other buffer, chunk j+2's x into registers, barrier
+        auto step = [&](int j, int sb) {
+            const u32x4 *const xs = smem + sb * BM * 8;
+            u32x4 af[MB];
+#pragma unroll
+            for (int m = 0; m < MB; ++m) af[m] = xs[xw_slot(16 * m + f_row, 4 * wk + (lane >> 4))];
+            const int jn = min(j + 1, npairs - 1);
+#pragma unroll
+            for (int pl = 0; pl < 3; ++pl)
+#pragma unroll
+                for (int n = 0; n < NBW; ++n) {
+                    const u32x4 b = wst[n][pl];
+#pragma unroll
+                    for (int m = 0; m < MB; ++m) acc[m][n] = mfma_bf16(af[m], b, acc[m][n]);
+                    wst[n][pl] = wfrag(jn, n, pl);
+                }
+            __builtin_amdgcn_sched_group_barrier(SG_DS_READ, MB, 0);
+#pragma unroll
+            for (int g = 0; g < 3 * NBW; ++g) {
+                __builtin_amdgcn_sched_group_barrier(SG_MFMA, MB, 0);
+                __builtin_amdgcn_sched_group_barrier(SG_VMEM_READ, 1, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            store_x(min(j + 1, npairs - 1), sb ^ 1, xst);
+            load_x(min(j + 2, npairs - 1), xst);
+            __syncthreads();
+        };
+        int j = 0;
+        for (; j + 2 <= npairs; j += 2) {
+            step(j, 0);
+            step(j + 1, 1);
+        }
+        if (j < npairs) step(j, 0);
+    }
+
+    // k-split hand-over through LDS (the staging buffers are dead: the last
+    // step ended with a barrier), then the partial logits of the tile.
+    constexpr int REGS = MB * NBW;
+    u32x4 *const red = smem + wn * REGS * 64 + lane;
+    if (wk == 1) {
+#pragma unroll
+        for (int m = 0; m < MB; ++m)
+#pragma unroll
+            for (int n = 0; n < NBW; ++n) red[(m * NBW + n) * 64] = __builtin_bit_cast(u32x4, acc[m][n]);
+    }
+    __syncthreads();
+    if (wk == 1) return;
+#pragma unroll
+    for (int m = 0; m < MB; ++m)
+#pragma unroll
+        for (int n = 0; n < NBW; ++n) acc[m][n] += __builtin_bit_cast(f32x4, red[(m * NBW + n) * 64]);
+    // accumulator r of block (m, n): token t0 + 16m + 4(l/16) + r, expert
+    // e0 + 16(NBW*wn + n) + l%16
+    float *const out = a.partial + (size_t)ks * a.T * a.E;
+#pragma unroll
+    for (int m = 0; m < MB; ++m)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int t = t0 + 16 * m + 4 * (lane >> 4) + r;
+            if (t < a.T) {
+#pragma unroll
+                for (int n = 0; n < NBW; ++n)
+                    out[(size_t)t * a.E + e0 + 16 * (NBW * wn + n) + f_row] = acc[m][n][r];
+            }
+        }
+}
+
 // Tile shapes: BM tokens x 64*NBW experts.
 struct X3Shape {
     int bm, nbw;
@@ -365,9 +549,9 @@ size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 template <int BM, int NBW>
 hipError_t launch_shape(const GateArgs &a, const GatePlan &p, hipStream_t stream)
 {
-    const dim3 grid(p.grid), block(256);
-    if (p.x3_presplit) return launch_kernel(x3_gemm_kernel<BM, NBW, X3_STAGES, false>, grid, block, stream, a);
-    return launch_kernel(x3_gemm_kernel<BM, NBW, X3_STAGES, true>, grid, block, stream, a);
+    const dim3 grid(p.grid);
+    if (p.x3_presplit) return launch_kernel(x3_gemm8_kernel<BM, NBW>, grid, dim3(512), stream, a);
+    return launch_kernel(x3_gemm_kernel<BM, NBW, X3_STAGES, true>, grid, dim3(256), stream, a);
 }
 
 }  // namespace
