@@ -80,6 +80,14 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is not built: run __graft_entry__.build() "
                            "or python -m sigmoid_group_limited_amd.build")
+    # The tensors and streams this binding passes come from PyTorch's HIP
+    # runtime.  Loading torch first makes the library bind to that same
+    # runtime; loaded first, it would bind to the system's copy, and a
+    # second runtime in the process cannot launch on torch's streams.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(path)
     vp, i32p, fp = ctypes.c_void_p, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_float)
     cfgp = ctypes.POINTER(siggate_cfg_t)

@@ -20,18 +20,18 @@
 // the float32 matrix cores, at 16x their per-instruction rate (3 products
 // per term: about 5x the arithmetic rate of the float32 route).
 //
-// Layout of the work.  A workgroup of 4 waves (one per SIMD) owns BM tokens
-// x BN = 64*NBW experts x one slice of the k range, and writes float32
-// partial logits [n_split, T, E]; the reduction of gate.hip adds the slices
-// in a fixed order and runs the selection.  Wave w owns experts
-// [16*NBW*w, 16*NBW*(w+1)) of the tile and all BM tokens, as MB = BM/16
-// token blocks x NBW expert blocks of 16x16 accumulators.  No W element is
-// used by two waves, so each wave loads its W fragments straight from global
-// memory into registers and splits them there (no LDS for W); x, shared by
-// the 4 waves, is staged in LDS as bfloat16 (32 k-columns per chunk,
-// double-buffered).  Global loads run P chunks ahead.  Tiles are ordered as
-// in the split GEMM of gate.hip: token tile fastest, and one contiguous run
-// of tiles per XCD, so the tiles that read one W slice share an L2.
+// Layout of the work.  A workgroup of 8 waves (two per SIMD: one wave per
+// SIMD cannot issue these MFMAs back to back at full rate) owns BM tokens x
+// BN = 64*NBW experts x one slice of the k range, and writes float32 partial
+// logits [n_split, T, E]; the reduction of gate.hip adds the slices in a
+// fixed order and runs the selection.  The waves are 4 expert quarters x 2
+// k-halves of every 64-column chunk, so no W element is loaded by two waves:
+// each wave loads its W fragments straight into registers (no LDS for W).
+// x, shared by the waves, is staged in LDS as bfloat16.  Large batches read
+// W as three bfloat16 planes split once per call by x3_split_w_kernel;
+// small batches split float32 W in registers.  Tiles are ordered as in the
+// split GEMM of gate.hip: token tile fastest, and one contiguous run of
+// tiles per XCD, so the tiles that read one W slice share an L2.
 #include "siggate_internal.h"
 
 namespace siggate {
@@ -112,234 +112,6 @@ __global__ __launch_bounds__(256) void x3_split_w_kernel(const float *W, uint16_
     out[2 * plane16 + i] = l;
 }
 
-// x pieces (16 bytes: 8 k-columns of one token) sit in LDS at row*64 bytes
-// plus a piece slot permuted by the row: rows 4 apart start 16 bytes apart,
-// so the 16 lanes of a fragment read (rows r..r+15, one k-piece) cover all
-// 64 banks once.
-__device__ __forceinline__ int x_slot(int row, int piece) { return row * 4 + (piece ^ ((row >> 2) & 3)); }
-
-// SPLIT: W fragments are loaded as float32 and split in registers (small
-// batches), or loaded as the three planes x3_split_w_kernel wrote (large
-// batches, where the same W slice is split once instead of once per token
-// tile and the matrix cores are not kept waiting on the split).
-template <int BM, int NBW, int P, bool SPLIT>
-__global__ __launch_bounds__(256) void x3_gemm_kernel(GateArgs a)
-{
-    constexpr int MB = BM / 16;              // token blocks per wave
-    constexpr int BN = 64 * NBW;             // experts per workgroup
-    constexpr int XP = BM * KC / 8 / 256;    // 8-element x pieces per thread per chunk
-    static_assert(KC == 32, "one chunk is one MFMA depth (32)");
-    static_assert(BM % 64 == 0 && XP >= 1, "every thread stages whole x pieces");
-    __shared__ __attribute__((aligned(16))) u32x4 xs[SPLIT ? 2 : 3][BM * KC / 8];
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    // Workgroup ids go round-robin over the 8 XCDs; each XCD gets one
-    // contiguous run of tile numbers (the grid is a multiple of 8).
-    const int q = (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
-    if (q >= a.n_tiles) return;   // padding of the grid (whole workgroup)
-    const int rq = q / a.t_tiles;
-    const int t0 = (q - rq * a.t_tiles) * BM;
-    const int ks = rq / a.e_tiles;
-    const int e0 = (rq - ks * a.e_tiles) * BN;
-    const int d = a.d;
-    const int c_begin = ks * a.chunks_per_split;
-    const int c_end = min(c_begin + a.chunks_per_split, a.chunks_total);
-
-    // W fragment of expert block n: lane l holds expert
-    // e0 + 16*(NBW*wave + n) + l%16, k-columns k0 + 8*(l/16) .. +7 (the
-    // operand layout of v_mfma_f32_16x16x32_bf16; x uses the same k order).
-    // Pieces past d (d is a multiple of 8) read the last in-range piece
-    // instead; their x is zero, so they add nothing.
-    const int f_row = lane & 15;
-    const int f_k = 8 * (lane >> 4);
-    // float32 W: row offsets; pre-split planes: this lane's 16 bytes in
-    // fragment (expert block, chunk 0) of plane 0, in 16-byte units
-    const int nc = a.chunks_total;
-    const size_t plane16 = (size_t)(a.E / 16) * nc * 64;
-    size_t wrow[NBW];
-#pragma unroll
-    for (int n = 0; n < NBW; ++n) {
-        const int eb = e0 / 16 + NBW * wave + n;
-        wrow[n] = SPLIT ? (size_t)(16 * eb + f_row) * d : (size_t)eb * nc * 64 + lane;
-    }
-    // x piece p = tid + 256*i: token row p/4, k-columns 8*(p%4) .. +7 of the
-    // chunk; rows past T read row T-1 (their logits are dropped).
-    const uint16_t *xrow[XP];
-    int xcol[XP], xdst[XP];
-#pragma unroll
-    for (int i = 0; i < XP; ++i) {
-        const int p = tid + 256 * i;
-        xrow[i] = a.x + (size_t)min(t0 + p / 4, a.T - 1) * d;
-        xcol[i] = 8 * (p % 4);
-        xdst[i] = x_slot(p / 4, p % 4);
-    }
-
-    auto load_x = [&](int c, u32x4 (&x)[XP]) {
-        const int k0 = c * KC;
-#pragma unroll
-        for (int i = 0; i < XP; ++i) x[i] = *(const u32x4 *)(xrow[i] + min(k0 + xcol[i], d - 8));
-    };
-    // Pieces past d are zeroed by a second store, in the last chunk only (a
-    // uniform branch), so that the common store waits on nothing but its own
-    // chunk's loads.
-    auto store_x = [&](int c, int buf, const u32x4 (&x)[XP]) {
-        const int k0 = c * KC;
-#pragma unroll
-        for (int i = 0; i < XP; ++i) xs[buf][xdst[i]] = x[i];
-        if (k0 + KC > d) {
-#pragma unroll
-            for (int i = 0; i < XP; ++i)
-                if (k0 + xcol[i] >= d) xs[buf][xdst[i]] = u32x4{0u, 0u, 0u, 0u};
-        }
-    };
-    auto read_a = [&](int buf, u32x4 (&f)[MB]) {
-#pragma unroll
-        for (int m = 0; m < MB; ++m) f[m] = xs[buf][x_slot(16 * m + f_row, lane >> 4)];
-    };
-
-    f32x4 acc[MB][NBW];
-#pragma unroll
-    for (int m = 0; m < MB; ++m)
-#pragma unroll
-        for (int n = 0; n < NBW; ++n) acc[m][n] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-
-    constexpr int SG_MFMA = 0x008, SG_VMEM_READ = 0x020, SG_DS_READ = 0x100, SG_DS_WRITE = 0x200;
-    if (c_begin < c_end) {
-        const int c_last = c_end - 1;
-        const int cb = c_begin;
-        const int nch = c_end - c_begin;
-        if constexpr (SPLIT) {
-            // float32 W in P register stages; x double-buffered in LDS.  One
-            // chunk: A fragments from LDS, the split of this chunk's W, the
-            // refill of its stage with chunk c+P, 3*MB*NBW MFMAs, then chunk
-            // c+1's x into the other buffer and the barrier that publishes it.
-            struct Stage {
-                f32x4 w[NBW][2];
-                u32x4 x[XP];
-            };
-            auto load_global = [&](int c, Stage &st) {
-                const int wk = min(c * KC + f_k, d - 8);
-#pragma unroll
-                for (int n = 0; n < NBW; ++n) {
-                    st.w[n][0] = *(const f32x4 *)(a.W + wrow[n] + wk);
-                    st.w[n][1] = *(const f32x4 *)(a.W + wrow[n] + wk + 4);
-                }
-                load_x(c, st.x);
-            };
-            auto step = [&](int c, int buf, Stage &cur, const Stage &next) {
-                u32x4 af[MB];
-                read_a(buf, af);
-                u32x4 bw[3][NBW];
-#pragma unroll
-                for (int n = 0; n < NBW; ++n) split3(cur.w[n][0], cur.w[n][1], bw[0][n], bw[1][n], bw[2][n]);
-                load_global(min(c + P, c_last), cur);
-#pragma unroll
-                for (int pl = 0; pl < 3; ++pl)
-#pragma unroll
-                    for (int n = 0; n < NBW; ++n)
-#pragma unroll
-                        for (int m = 0; m < MB; ++m) acc[m][n] = mfma_bf16(af[m], bw[pl][n], acc[m][n]);
-                store_x(min(c + 1, c_last), buf ^ 1, next.x);
-                __syncthreads();
-            };
-            Stage st[P];
-#pragma unroll
-            for (int j = 0; j < P; ++j) load_global(min(cb + j, c_last), st[j]);
-            store_x(cb, 0, st[0].x);
-            __syncthreads();
-            // local chunk i uses LDS buffer i%2 and stage i%P: unrolled by
-            // lcm(P, 2) so that both stay static
-            constexpr int U = P % 2 ? 2 * P : P;
-            int i = 0;
-            for (; i + U <= nch; i += U) {
-#pragma unroll
-                for (int u = 0; u < U; ++u) step(cb + i + u, u & 1, st[u % P], st[(u + 1) % P]);
-            }
-#pragma unroll
-            for (int u = 0; u < U - 1; ++u)
-                if (i + u < nch) step(cb + i + u, u & 1, st[u % P], st[(u + 1) % P]);
-        } else {
-            // Pre-split planes.  Local chunk i: MFMAs on A fragments af[i%2]
-            // (read during chunk i-1) and W fragments wst[i%2] (each refilled
-            // with chunk i+2 right after its last MFMA, so the loads spread
-            // one per MB MFMAs); meanwhile the A fragments of chunk i+1 come
-            // from LDS buffer (i+1)%3, and x of chunk i+2 (loaded two chunks
-            // earlier) goes to buffer (i+2)%3.  With x three-buffered, no
-            // MFMA waits on an LDS read issued in its own chunk, and the one
-            // barrier per chunk publishes chunk i+2 two chunks ahead.
-            u32x4 wst[2][NBW][3];
-            u32x4 xst[2][XP];
-            u32x4 af[2][MB];
-            const u32x4 *const planes = (const u32x4 *)a.w_planes;
-            auto load_w = [&](int c, u32x4 (&w)[NBW][3]) {
-#pragma unroll
-                for (int n = 0; n < NBW; ++n)
-#pragma unroll
-                    for (int pl = 0; pl < 3; ++pl) w[n][pl] = planes[pl * plane16 + wrow[n] + (size_t)c * 64];
-            };
-            load_w(cb, wst[0]);
-            load_w(min(cb + 1, c_last), wst[1]);
-            load_x(cb, xst[0]);
-            load_x(min(cb + 1, c_last), xst[1]);
-            store_x(cb, 0, xst[0]);
-            store_x(min(cb + 1, c_last), 1, xst[1]);
-            load_x(min(cb + 2, c_last), xst[0]);
-            load_x(min(cb + 3, c_last), xst[1]);
-            __syncthreads();
-            read_a(0, af[0]);
-            auto pstep = [&](int i, int ab, int sb) {   // ab = i % 3, sb = i % 2
-                const int c = cb + i;
-                read_a((ab + 1) % 3, af[sb ^ 1]);
-                const int cw = min(c + 2, c_last);
-#pragma unroll
-                for (int pl = 0; pl < 3; ++pl)
-#pragma unroll
-                    for (int n = 0; n < NBW; ++n) {
-                        const u32x4 b = wst[sb][n][pl];
-#pragma unroll
-                        for (int m = 0; m < MB; ++m) acc[m][n] = mfma_bf16(af[sb][m], b, acc[m][n]);
-                        wst[sb][n][pl] = planes[pl * plane16 + wrow[n] + (size_t)cw * 64];
-                    }
-                __builtin_amdgcn_sched_group_barrier(SG_DS_READ, MB, 0);
-#pragma unroll
-                for (int g = 0; g < 3 * NBW; ++g) {
-                    __builtin_amdgcn_sched_group_barrier(SG_MFMA, MB, 0);
-                    __builtin_amdgcn_sched_group_barrier(SG_VMEM_READ, 1, 0);
-                }
-                __builtin_amdgcn_sched_barrier(0);
-                store_x(min(c + 2, c_last), (ab + 2) % 3, xst[sb]);
-                load_x(min(c + 4, c_last), xst[sb]);
-                __syncthreads();
-            };
-            int i = 0;
-            for (; i + 6 <= nch; i += 6) {
-#pragma unroll
-                for (int u = 0; u < 6; ++u) pstep(i + u, u % 3, u & 1);
-            }
-#pragma unroll
-            for (int u = 0; u < 5; ++u)
-                if (i + u < nch) pstep(i + u, u % 3, u & 1);
-        }
-    }
-
-    // Accumulator r of block (m, n) in lane l: token t0 + 16m + 4(l/16) + r,
-    // expert e0 + 16(NBW*wave + n) + l%16.
-    float *const out = a.partial + (size_t)ks * a.T * a.E;
-#pragma unroll
-    for (int m = 0; m < MB; ++m)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int t = t0 + 16 * m + 4 * (lane >> 4) + r;
-            if (t < a.T) {
-#pragma unroll
-                for (int n = 0; n < NBW; ++n)
-                    out[(size_t)t * a.E + e0 + 16 * (NBW * wave + n) + f_row] = acc[m][n][r];
-            }
-        }
-}
-
 // Large batches: the pre-split planes on 8 waves (two per SIMD -- one wave
 // per SIMD cannot issue these MFMAs back to back at full rate).  The waves
 // are 4 expert quarters (16*NBW experts each) x 2 k-halves: a chunk is 64
@@ -369,7 +141,10 @@ struct X3Wide {
 // 64 banks once.
 __device__ __forceinline__ int xw_slot(int row, int piece) { return row * 8 + (piece ^ ((row >> 1) & 7)); }
 
-template <int BM, int NBW>
+// SPLIT: W fragments are loaded as float32 (row-major W) and split in
+// registers (small batches: no extra launch, no planes); otherwise they are
+// loaded from the fragment-ordered planes of x3_split_w_kernel.
+template <int BM, int NBW, bool SPLIT>
 __global__ __launch_bounds__(512) void x3_gemm8_kernel(GateArgs a)
 {
     using S = X3Wide<BM, NBW>;
@@ -397,15 +172,27 @@ __global__ __launch_bounds__(512) void x3_gemm8_kernel(GateArgs a)
     const int f_row = lane & 15;
     const size_t plane16 = (size_t)(a.E / 16) * nc * 64;
     const u32x4 *const planes = (const u32x4 *)a.w_planes;
+    // this lane's expert row: e0 + 16(NBW*wn + n) + l%16, k-columns
+    // 8*(l/16) .. +7 of a 32-column fragment
     size_t wbase[NBW];
 #pragma unroll
-    for (int n = 0; n < NBW; ++n) wbase[n] = (size_t)(e0 / 16 + NBW * wn + n) * nc * 64 + lane;
+    for (int n = 0; n < NBW; ++n) {
+        const int eb = e0 / 16 + NBW * wn + n;
+        wbase[n] = SPLIT ? (size_t)(16 * eb + f_row) * d : (size_t)eb * nc * 64 + lane;
+    }
     // W fragment (plane pl, block n) of 64-column chunk j: 32-column
     // fragment c_begin + 2j + wk (clamped; a fragment past the slice or past
     // d meets zero x)
     auto wfrag = [&](int j, int n, int pl) {
         const int c = min(c_begin + 2 * j + wk, c_last);
         return planes[pl * plane16 + wbase[n] + (size_t)c * 64];
+    };
+    // the same fragment as 8 float32 (SPLIT), pieces past d clamped
+    auto wfrag32 = [&](int j, int n, f32x4 (&w)[2]) {
+        const int c = min(c_begin + 2 * j + wk, c_last);
+        const float *const p = a.W + wbase[n] + min(c * KC + 8 * (lane >> 4), d - 8);
+        w[0] = *(const f32x4 *)p;
+        w[1] = *(const f32x4 *)(p + 4);
     };
     // x piece i of this thread: row tid/8 + 64i, k-piece tid%8 of the chunk
     const int kp = tid & 7;
@@ -445,51 +232,106 @@ __global__ __launch_bounds__(512) void x3_gemm8_kernel(GateArgs a)
 
     constexpr int SG_MFMA = 0x008, SG_VMEM_READ = 0x020, SG_DS_READ = 0x100;
     if (npairs > 0) {
-        u32x4 wst[NBW][3];
-        u32x4 xst[XQ];
+        if constexpr (SPLIT) {
+            // Small batches: a step is a few MFMAs, so loads run PW chunks
+            // ahead in register rings (W as float32, x as bfloat16) to cover
+            // first-touch memory latency.  Chunk j: A fragments from buffer
+            // j%2, the split of W slot j%PW (refilled with chunk j+PW), the
+            // MFMAs, then chunk j+1's x into the other buffer (its slot
+            // refilled with chunk j+1+PW) and the barrier.
+            constexpr int PW = BM == 64 ? 4 : 2;
+            f32x4 wr[PW][NBW][2];
+            u32x4 xr[PW][XQ];
 #pragma unroll
-        for (int n = 0; n < NBW; ++n)
+            for (int u = 0; u < PW; ++u) {
 #pragma unroll
-            for (int pl = 0; pl < 3; ++pl) wst[n][pl] = wfrag(0, n, pl);
-        load_x(0, xst);
-        store_x(0, 0, xst);
-        load_x(min(1, npairs - 1), xst);
-        __syncthreads();
-        // chunk j: A fragments from buffer j%2, MFMAs on the W fragments
-        // (each refilled with chunk j+1 after its last use), chunk j+1's x
-        // into the other buffer, chunk j+2's x into registers, barrier
-        auto step = [&](int j, int sb) {
-            const u32x4 *const xs = smem + sb * BM * 8;
-            u32x4 af[MB];
+                for (int n = 0; n < NBW; ++n) wfrag32(min(u, npairs - 1), n, wr[u][n]);
+                load_x(min(u, npairs - 1), xr[u]);
+            }
+            store_x(0, 0, xr[0]);
+            load_x(min(PW, npairs - 1), xr[0]);
+            __syncthreads();
+            auto step = [&](int j, int u) {   // u = j % PW; PW is even, so j%2 = u%2
+                const int sb = u & 1;
+                const u32x4 *const xs = smem + sb * BM * 8;
+                u32x4 af[MB];
 #pragma unroll
-            for (int m = 0; m < MB; ++m) af[m] = xs[xw_slot(16 * m + f_row, 4 * wk + (lane >> 4))];
-            const int jn = min(j + 1, npairs - 1);
-#pragma unroll
-            for (int pl = 0; pl < 3; ++pl)
+                for (int m = 0; m < MB; ++m) af[m] = xs[xw_slot(16 * m + f_row, 4 * wk + (lane >> 4))];
+                u32x4 bw[NBW][3];
 #pragma unroll
                 for (int n = 0; n < NBW; ++n) {
-                    const u32x4 b = wst[n][pl];
-#pragma unroll
-                    for (int m = 0; m < MB; ++m) acc[m][n] = mfma_bf16(af[m], b, acc[m][n]);
-                    wst[n][pl] = wfrag(jn, n, pl);
+                    split3(wr[u][n][0], wr[u][n][1], bw[n][0], bw[n][1], bw[n][2]);
+                    wfrag32(min(j + PW, npairs - 1), n, wr[u][n]);
                 }
-            __builtin_amdgcn_sched_group_barrier(SG_DS_READ, MB, 0);
 #pragma unroll
-            for (int g = 0; g < 3 * NBW; ++g) {
-                __builtin_amdgcn_sched_group_barrier(SG_MFMA, MB, 0);
-                __builtin_amdgcn_sched_group_barrier(SG_VMEM_READ, 1, 0);
+                for (int pl = 0; pl < 3; ++pl)
+#pragma unroll
+                    for (int n = 0; n < NBW; ++n)
+#pragma unroll
+                        for (int m = 0; m < MB; ++m) acc[m][n] = mfma_bf16(af[m], bw[n][pl], acc[m][n]);
+                __builtin_amdgcn_sched_barrier(0);
+                const int u1 = (u + 1) % PW;
+                store_x(min(j + 1, npairs - 1), sb ^ 1, xr[u1]);
+                load_x(min(j + 1 + PW, npairs - 1), xr[u1]);
+                __syncthreads();
+            };
+            int j = 0;
+            for (; j + PW <= npairs; j += PW) {
+#pragma unroll
+                for (int u = 0; u < PW; ++u) step(j + u, u);
             }
-            __builtin_amdgcn_sched_barrier(0);
-            store_x(min(j + 1, npairs - 1), sb ^ 1, xst);
-            load_x(min(j + 2, npairs - 1), xst);
+#pragma unroll
+            for (int u = 0; u < PW - 1; ++u)
+                if (j + u < npairs) step(j + u, u);
+        } else {
+            // Large batches: a step is 3*MB*NBW MFMAs per wave, long enough
+            // for a one-chunk refill of each W fragment after its last use.
+            u32x4 wst[NBW][3];
+            u32x4 xst[XQ];
+#pragma unroll
+            for (int n = 0; n < NBW; ++n)
+#pragma unroll
+                for (int pl = 0; pl < 3; ++pl) wst[n][pl] = wfrag(0, n, pl);
+            load_x(0, xst);
+            store_x(0, 0, xst);
+            load_x(min(1, npairs - 1), xst);
             __syncthreads();
-        };
-        int j = 0;
-        for (; j + 2 <= npairs; j += 2) {
-            step(j, 0);
-            step(j + 1, 1);
+            // chunk j: A fragments from buffer j%2, MFMAs on the W fragments
+            // (each refilled with chunk j+1 after its last use), chunk j+1's
+            // x into the other buffer, chunk j+2's x into registers, barrier
+            auto step = [&](int j, int sb) {
+                const u32x4 *const xs = smem + sb * BM * 8;
+                u32x4 af[MB];
+#pragma unroll
+                for (int m = 0; m < MB; ++m) af[m] = xs[xw_slot(16 * m + f_row, 4 * wk + (lane >> 4))];
+                const int jn = min(j + 1, npairs - 1);
+#pragma unroll
+                for (int pl = 0; pl < 3; ++pl)
+#pragma unroll
+                    for (int n = 0; n < NBW; ++n) {
+                        const u32x4 b = wst[n][pl];
+#pragma unroll
+                        for (int m = 0; m < MB; ++m) acc[m][n] = mfma_bf16(af[m], b, acc[m][n]);
+                        wst[n][pl] = wfrag(jn, n, pl);
+                    }
+                __builtin_amdgcn_sched_group_barrier(SG_DS_READ, MB, 0);
+#pragma unroll
+                for (int g = 0; g < 3 * NBW; ++g) {
+                    __builtin_amdgcn_sched_group_barrier(SG_MFMA, MB, 0);
+                    __builtin_amdgcn_sched_group_barrier(SG_VMEM_READ, 1, 0);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                store_x(min(j + 1, npairs - 1), sb ^ 1, xst);
+                load_x(min(j + 2, npairs - 1), xst);
+                __syncthreads();
+            };
+            int j = 0;
+            for (; j + 2 <= npairs; j += 2) {
+                step(j, 0);
+                step(j + 1, 1);
+            }
+            if (j < npairs) step(j, 0);
         }
-        if (j < npairs) step(j, 0);
     }
 
     // k-split hand-over through LDS (the staging buffers are dead: the last
@@ -538,7 +380,6 @@ constexpr double X3_CHUNK_OVERHEAD = 150.0;
 constexpr double X3_LATENCY = 3000.0;
 constexpr double X3_BYTES_PER_CYCLE = 2400.0;
 constexpr int X3_N_CU = 256;
-constexpr int X3_STAGES = 3;
 // From this many tokens on, W is split once per call into planes (the split
 // kernel reads W once and writes 1.5x its bytes) instead of in registers by
 // every token tile.
@@ -550,8 +391,8 @@ template <int BM, int NBW>
 hipError_t launch_shape(const GateArgs &a, const GatePlan &p, hipStream_t stream)
 {
     const dim3 grid(p.grid);
-    if (p.x3_presplit) return launch_kernel(x3_gemm8_kernel<BM, NBW>, grid, dim3(512), stream, a);
-    return launch_kernel(x3_gemm_kernel<BM, NBW, X3_STAGES, true>, grid, dim3(256), stream, a);
+    if (p.x3_presplit) return launch_kernel(x3_gemm8_kernel<BM, NBW, false>, grid, dim3(512), stream, a);
+    return launch_kernel(x3_gemm8_kernel<BM, NBW, true>, grid, dim3(512), stream, a);
 }
 
 }  // namespace
@@ -562,9 +403,12 @@ GatePlan plan_x3(int T, int d, int E)
     p.split = true;
     const int chunks = (d + KC - 1) / KC;
     double best = 1e300;
+    const bool presplit = T >= X3_PRESPLIT_MIN_T;
     for (const X3Shape &sh : X3_SHAPES) {
         const int bn = 64 * sh.nbw;
         if (E % bn != 0) continue;
+        // the in-register split of a 128 x 192 tile does not fit 256 VGPRs
+        if (!presplit && sh.bm == 128 && sh.nbw == 3) continue;
         const long tiles = ((long)T + sh.bm - 1) / sh.bm * (E / bn);
         const double chunk_cost = 3.0 * (sh.bm / 16) * sh.nbw * 16.0 + X3_CHUNK_OVERHEAD;
         for (int s = 1; s <= chunks; ++s) {
@@ -588,7 +432,7 @@ GatePlan plan_x3(int T, int d, int E)
     const long n = (long)p.t_tiles * p.e_tiles * p.n_split;
     p.grid = (int)((n + 7) / 8 * 8);
     p.m_blocks = 0;
-    p.x3_presplit = T >= X3_PRESPLIT_MIN_T;
+    p.x3_presplit = presplit;
     const size_t partials = (size_t)p.n_split * (size_t)T * (size_t)E * sizeof(float);
     p.planes_offset = p.x3_presplit ? align256(partials) : 0;
     // planes: 3 x E x (chunks * 32) bfloat16
