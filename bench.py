@@ -65,6 +65,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_FP32_MFMA_TFLOPS = 157.3   # MI355X dense fp32 matrix peak
 PEAK_HBM_GBS = 8000.0           # MI355X HBM3E peak
+PEAK_BF16_MFMA_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
 GATE_SOURCE = os.path.join(ROOT, "sigmoid_group_limited_amd", "csrc", "gate.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gate_traffic.json")
 
@@ -288,9 +289,6 @@ def overlap_line(name: str, steps: int, warmup: int):
                     "not the step of value"}
 
 
-PEAK_BF16_MFMA_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
-
-
 def bf16x3_line(name: str, steps: int, warmup: int, ref_indices=None):
     """The same step with the logits on the bfloat16 three-way route
     (cfg.logits_path = 1: W split exactly into three bfloat16 parts, three
@@ -435,6 +433,9 @@ def main():
                     help="skip the two-stream run of two independent batches")
     ap.add_argument("--no-bf16x3", action="store_true",
                     help="skip the lines of the bfloat16 three-way logits route")
+    ap.add_argument("--logits-path", type=int, choices=(0, 1), default=0,
+                    help="logits route of the main step: 0 float32 MFMA (default), "
+                         "1 the bfloat16 three-way route (then its roofline is bf16)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (counter calibration)")
     args = ap.parse_args()
@@ -461,12 +462,16 @@ def main():
         print(json.dumps({"copy_bytes": n, "launches": 3}))
         return
 
-    case = Case(args.workload)
+    lp = args.logits_path
+    case = Case(args.workload, lp)
     ms, gate_ms, disp_ms = case.run(args.steps, args.warmup)
     T = case.w.T
     flops, gate_bytes, disp_bytes = case.algorithmic()
-    achieved = flops / (gate_ms * 1e-3) / 1e12
-    traffic = gate_traffic(case.w.name, gate_bytes)
+    # the bfloat16 three-way route executes 3 bf16 products per term
+    mfma_flops = flops if lp == 0 else 3 * flops
+    peak = PEAK_FP32_MFMA_TFLOPS if lp == 0 else PEAK_BF16_MFMA_TFLOPS
+    achieved = mfma_flops / (gate_ms * 1e-3) / 1e12
+    traffic = gate_traffic(case.w.name, gate_bytes) if lp == 0 else None
     result = {
         "metric": "routed tokens/s (gate+dispatch)",
         "value": T / (ms * 1e-3),
@@ -478,22 +483,22 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "f32" if lp == 0 else "bf16x3 products, f32 accumulation",
         "data": "synthetic (seeded; x ~ N(0,1) in bfloat16, W ~ N(0,1/d), bias ~ U(-0.05,0.05))",
         "config": {"workload": case.w.name, "T": T, "d": case.w.d, "E": case.cfg.E,
                    "n_group": case.cfg.n_group, "topk_group": case.cfg.topk_group,
                    "top_k": case.cfg.top_k, "route_scale": case.cfg.route_scale,
-                   "parallelism": "single GPU"},
-        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_FP32_MFMA_TFLOPS,
-                     "unit": "TFLOP/s", "frac": achieved / PEAK_FP32_MFMA_TFLOPS,
+                   "parallelism": "single GPU", "logits_path": lp},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak,
+                     "unit": "TFLOP/s", "frac": achieved / peak,
                      "traffic": traffic},
         "stages": {
             "gate_ms": gate_ms, "dispatch_ms": disp_ms,
-            "gate_tflops": achieved,
+            "gate_tflops": flops / (gate_ms * 1e-3) / 1e12,
             "dispatch_algorithmic_GBps": disp_bytes / (disp_ms * 1e-3) / 1e9,
             "dispatch_hbm_frac": disp_bytes / (disp_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
             "pairs_per_s": T * case.cfg.top_k / (ms * 1e-3),
-            "roofline_tokens_per_s": T / (flops / (PEAK_FP32_MFMA_TFLOPS * 1e12)
+            "roofline_tokens_per_s": T / (mfma_flops / (peak * 1e12)
                                           + disp_bytes / (PEAK_HBM_GBS * 1e9)),
         },
     }
@@ -506,14 +511,14 @@ def main():
                           "note": "1 GiB scrub written before each step"}
     result["after_path"] = case.run_next_rows(max(3, args.steps // 2), 2)
     if args.secondary:
-        sec = Case(args.secondary)
+        sec = Case(args.secondary, lp)
         ms2, g2, d2 = sec.run(args.steps, args.warmup)
         f2, _, db2 = sec.algorithmic()
         result["secondary"] = {
             "workload": sec.w.name, "E": sec.cfg.E, "value": sec.w.T / (ms2 * 1e-3),
             "ms_per_step": ms2, "gate_ms": g2, "dispatch_ms": d2,
             "gate_tflops": f2 / (g2 * 1e-3) / 1e12,
-            "gate_mfma_frac": f2 / (g2 * 1e-3) / 1e12 / PEAK_FP32_MFMA_TFLOPS,
+            "gate_mfma_frac": (f2 if lp == 0 else 3 * f2) / (g2 * 1e-3) / 1e12 / peak,
             "dispatch_algorithmic_GBps": db2 / (d2 * 1e-3) / 1e9,
             "variants": sec.run_variants(max(5, args.steps // 2), 2),
         }
@@ -521,8 +526,9 @@ def main():
     if not args.no_overlap:
         result["overlap"] = overlap_line(args.workload, max(8, args.steps), 2)
     if not args.no_decode:
-        result["decode"] = [decode_line("kimi-k2-decode"), decode_line("dsv3-tiny")]
-    if not args.no_bf16x3:
+        result["decode"] = [decode_line("kimi-k2-decode", logits_path=lp),
+                            decode_line("dsv3-tiny", logits_path=lp)]
+    if not args.no_bf16x3 and lp == 0:
         ref = case.indices.clone()
         x3 = {"default": bf16x3_line(args.workload, args.steps, args.warmup, ref)}
         if args.secondary:

@@ -158,10 +158,22 @@ __global__ __launch_bounds__(512) void x3_gemm8_kernel(GateArgs a)
     const int wk = wave >> 2;         // k-half of every chunk
     const int q = (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
     if (q >= a.n_tiles) return;       // padding of the grid (whole workgroup)
-    const int rq = q / a.t_tiles;
-    const int t0 = (q - rq * a.t_tiles) * BM;
-    const int ks = rq / a.e_tiles;
-    const int e0 = (rq - ks * a.e_tiles) * S::BN;
+    // Tile numbers run token tile fastest (the token tiles that read one W
+    // slice share an XCD's L2: small batches, where W dominates), or expert
+    // tile fastest (the expert tiles of one token tile share it, so x, which
+    // dominates large batches, crosses from HBM once)
+    int t0, e0, ks;
+    if (a.e_fast) {
+        const int rq = q / a.e_tiles;
+        e0 = (q - rq * a.e_tiles) * S::BN;
+        ks = rq / a.t_tiles;
+        t0 = (rq - ks * a.t_tiles) * BM;
+    } else {
+        const int rq = q / a.t_tiles;
+        t0 = (q - rq * a.t_tiles) * BM;
+        ks = rq / a.e_tiles;
+        e0 = (rq - ks * a.e_tiles) * S::BN;
+    }
     const int d = a.d;
     const int nc = a.chunks_total;                       // 32-column fragments per row
     const int c_begin = ks * a.chunks_per_split;         // in 32-column units
@@ -444,6 +456,7 @@ GatePlan plan_x3(int T, int d, int E)
 hipError_t launch_x3_gemm(const GateArgs &args, const GatePlan &p, hipStream_t stream)
 {
     GateArgs a = args;
+    a.e_fast = p.x3_presplit ? 1 : 0;
     if (p.x3_presplit) {
         uint16_t *planes = (uint16_t *)((char *)a.partial + p.planes_offset);
         const size_t n_lanes = (size_t)(a.E / 16) * a.chunks_total * 64;

@@ -46,6 +46,7 @@ struct GateArgs {
     int n_split;            // k-slices (1 = whole k range in one workgroup)
     int t_tiles, e_tiles;   // token and expert tiles of the split GEMM
     int n_tiles;            // t_tiles * e_tiles * n_split
+    int e_fast;             // x3 tiles: expert tile fastest (1) or token tile fastest (0)
     float *weights;         // [T, top_k]      (MODE_SELECT)
     int32_t *indices;       // [T, top_k]      (MODE_SELECT)
     float *logits;          // [T, E]          (MODE_LOGITS)
