@@ -3,7 +3,9 @@
 // dispatch and the combine on a synthetic batch, checks of what the results
 // must satisfy, and event timing of gate + dispatch.
 //
-//   route_c [kimi|dsv3] [T] [d]        (defaults: kimi 256 7168)
+//   route_c [kimi|dsv3] [T] [d] [fp32|x3]   (defaults: kimi 256 7168 fp32)
+//
+// x3 selects the bfloat16 three-way logits route (cfg.logits_path = 1).
 //
 // Exit status 0 when every check holds.  One line of JSON on stdout.
 #include <hip/hip_runtime.h>
@@ -84,6 +86,7 @@ int main(int argc, char **argv)
     const bool dsv3 = argc > 1 && strcmp(argv[1], "dsv3") == 0;
     const int T = argc > 2 ? atoi(argv[2]) : 256;
     const int d = argc > 3 ? atoi(argv[3]) : 7168;
+    const bool x3 = argc > 4 && strcmp(argv[4], "x3") == 0;
     siggate_cfg_t cfg;
     memset(&cfg, 0, sizeof cfg);
     cfg.T = T;
@@ -93,6 +96,7 @@ int main(int argc, char **argv)
     cfg.topk_group = dsv3 ? 4 : 1;
     cfg.top_k = 8;
     cfg.route_scale = dsv3 ? 2.5f : 2.827f;
+    cfg.logits_path = x3 ? 1 : 0;
     const int E = cfg.E, K = cfg.top_k;
     const size_t n_pairs = (size_t)T * K;
 
@@ -198,8 +202,8 @@ int main(int argc, char **argv)
     float ms = 0.0f;
     HIP_OK(hipEventElapsedTime(&ms, e0, e1));
     const double us = ms * 1e3 / 20;
-    printf("{\"model\": \"%s\", \"T\": %d, \"d\": %d, \"E\": %d, \"checks_failed\": %d, "
-           "\"gate_dispatch_us\": %.2f, \"tokens_per_s\": %.0f}\n",
-           dsv3 ? "dsv3" : "kimi", T, d, E, failures, us, T / (us * 1e-6));
+    printf("{\"model\": \"%s\", \"T\": %d, \"d\": %d, \"E\": %d, \"logits_path\": %d, "
+           "\"checks_failed\": %d, \"gate_dispatch_us\": %.2f, \"tokens_per_s\": %.0f}\n",
+           dsv3 ? "dsv3" : "kimi", T, d, E, cfg.logits_path, failures, us, T / (us * 1e-6));
     return failures ? 1 : 0;
 }

@@ -46,15 +46,17 @@ VARIANTS = [
 
 
 @pytest.mark.parametrize("name,gc,T,d,opts,bias_kind", VARIANTS, ids=[v[0] for v in VARIANTS])
-def test_gate_variant(o, name, gc, T, d, opts, bias_kind):
-    say(f"[variant] {name}")
+@pytest.mark.parametrize("lp", [0, 1], ids=["fp32", "bf16x3"])
+def test_gate_variant(o, name, gc, T, d, opts, bias_kind, lp):
+    """Each variant on both logits routes (the selection is shared)."""
+    say(f"[variant] {name} logits_path={lp}")
     gi = wl.make_gate_inputs(T, d, gc, seed=T + 7)
     bias = None if bias_kind == "none" else gi.bias
     if bias_kind == "negative":
         # most choice scores below zero: a 0.0 fill then beats kept experts
         bias = (gi.bias - np.float32(0.9)).astype(np.float32)
     cfg = dataclasses.replace(sg.Cfg(T, d, gc.n_experts, gc.n_group, gc.topk_group, gc.top_k,
-                                     gc.route_scale), **opts)
+                                     gc.route_scale, logits_path=lp), **opts)
     x, W, _ = dev_inputs(gi)
     b = None if bias is None else torch.from_numpy(bias).cuda()
     w, i = sg.siggate_forward(x, W, b, cfg)
