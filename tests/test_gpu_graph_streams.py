@@ -55,9 +55,11 @@ def _snapshot(bufs):
 @pytest.mark.parametrize("gc,T,d", [(wl.KIMI_K2, 256, 7168), (wl.DSV3, 64, 7168),
                                     (wl.DSV3, 2048, 1024), (wl.KIMI_K2, 16384, 512)],
                          ids=["kimi_T256", "dsv3_T64", "dsv3_T2048", "kimi_T16384"])
-def test_graph_replay_matches_eager(gc, T, d):
-    say(f"[graph] E={gc.n_experts} T={T} d={d}")
-    cfg = sg.Cfg(T, d, gc.n_experts, gc.n_group, gc.topk_group, gc.top_k, gc.route_scale)
+@pytest.mark.parametrize("lp", [0, 1], ids=["fp32", "bf16x3"])
+def test_graph_replay_matches_eager(gc, T, d, lp):
+    say(f"[graph] E={gc.n_experts} T={T} d={d} logits_path={lp}")
+    cfg = sg.Cfg(T, d, gc.n_experts, gc.n_group, gc.topk_group, gc.top_k, gc.route_scale,
+                 logits_path=lp)
     inputs = [wl.make_gate_inputs(T, d, gc, seed=s) for s in (21, 22, 23)]
     x = torch.empty((T, d), dtype=torch.bfloat16, device="cuda")
     W = torch.from_numpy(inputs[0].W).cuda()
@@ -85,12 +87,13 @@ def test_graph_replay_matches_eager(gc, T, d):
             assert torch.equal(a, c), f"replay {rep}: output {k} differs from the eager call"
 
 
-def test_concurrent_streams_match_sequential():
+@pytest.mark.parametrize("lp", [0, 1], ids=["fp32", "bf16x3"])
+def test_concurrent_streams_match_sequential(lp):
     """Independent batches on two streams at once, each with its own
     workspace and outputs, give exactly the sequential results."""
     gc = wl.DSV3
-    cfgs = [sg.Cfg(T, 7168, gc.n_experts, gc.n_group, gc.topk_group, gc.top_k, gc.route_scale)
-            for T in (16384, 256)]
+    cfgs = [sg.Cfg(T, 7168, gc.n_experts, gc.n_group, gc.topk_group, gc.top_k, gc.route_scale,
+                   logits_path=lp) for T in (16384, 256)]
     gis = [wl.make_gate_inputs(c.T, 7168, gc, seed=31 + k) for k, c in enumerate(cfgs)]
     xs = [torch.from_numpy(g.x.view(np.int16)).cuda().view(torch.bfloat16) for g in gis]
     W = torch.from_numpy(gis[0].W).cuda()
