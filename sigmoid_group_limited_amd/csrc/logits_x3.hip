@@ -404,7 +404,9 @@ hipError_t launch_shape(const GateArgs &a, const GatePlan &p, hipStream_t stream
 {
     const dim3 grid(p.grid);
     if (p.x3_presplit) return launch_kernel(x3_gemm8_kernel<BM, NBW, false>, grid, dim3(512), stream, a);
-    return launch_kernel(x3_gemm8_kernel<BM, NBW, true>, grid, dim3(512), stream, a);
+    // (the plan never splits a 128 x 192 tile in registers: it would not fit)
+    if constexpr (BM == 128 && NBW == 3) return hipErrorInvalidValue;
+    else return launch_kernel(x3_gemm8_kernel<BM, NBW, true>, grid, dim3(512), stream, a);
 }
 
 }  // namespace
