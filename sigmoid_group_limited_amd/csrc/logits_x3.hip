@@ -112,19 +112,18 @@ __global__ __launch_bounds__(256) void x3_split_w_kernel(const float *W, uint16_
     out[2 * plane16 + i] = l;
 }
 
-// Large batches: the pre-split planes on 8 waves (two per SIMD -- one wave
-// per SIMD cannot issue these MFMAs back to back at full rate).  The waves
-// are 4 expert quarters (16*NBW experts each) x 2 k-halves: a chunk is 64
-// k-columns and wave (wn, wk) takes its 32-column half wk, so every W
-// fragment is still loaded by exactly one wave.  x is staged in LDS 64
-// columns (128 bytes of a row) at a time, 8 threads per row (whole cache
-// lines), double-buffered.  Each wave holds its W fragments for two chunks
-// in registers and refills each one right after its last MFMA.  At the end
-// the k-half-1 wave of each quarter hands its sums to the k-half-0 wave
-// through LDS, which adds them after its own (a fixed order) and writes the
-// partial logits.  (Each wave's W fragments are refilled with the next chunk
-// in the order they are consumed, so one register buffer gives every load a
-// whole chunk of MFMA work to land in.)
+// The GEMM on 8 waves (two per SIMD -- one wave per SIMD cannot issue these
+// MFMAs back to back at full rate).  The waves are 4 expert quarters
+// (16*NBW experts each) x 2 k-halves: a chunk is 64 k-columns and wave
+// (wn, wk) takes its 32-column half wk, so every W fragment is loaded by
+// exactly one wave.  x is staged in LDS 64 columns (128 bytes of a row) at a
+// time, 8 threads per row (whole cache lines), double-buffered.  Each wave
+// holds one chunk of W fragments in registers and refills each with the next
+// chunk right after its last MFMA, in the order they are consumed, so every
+// load has a whole chunk of MFMA work to land in (small batches, whose
+// chunks are short, run a deeper ring instead).  At the end the k-half-1 wave
+// of each quarter hands its sums to the k-half-0 wave through LDS, which adds
+// them after its own (a fixed order) and writes the partial logits.
 template <int BM, int NBW>
 struct X3Wide {
     static constexpr int MB = BM / 16;               // token blocks per wave
