@@ -394,7 +394,7 @@ constexpr int X3_N_CU = 256;
 // From this many tokens on, W is split once per call into planes (the split
 // kernel reads W once and writes 1.5x its bytes) instead of in registers by
 // every token tile.
-constexpr int X3_PRESPLIT_MIN_T = 4096;
+constexpr int X3_PRESPLIT_MIN_T = 1024;
 
 size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 
