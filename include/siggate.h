@@ -99,7 +99,10 @@ typedef enum siggate_status {
 /* Bytes of device workspace that siggate_forward and siggate_dispatch need
  * for this configuration: the larger of the two needs, counting only a call
  * that accepts the configuration (0 if neither does; 0 is also possible for
- * an accepted configuration). */
+ * an accepted configuration).  It depends on logits_path: route 1 always
+ * needs float32 partial logits (n_split x T x E), and from T = 1024 on also
+ * the three bfloat16 planes of W (3 x E x d rounded up to 32 columns, x 2
+ * bytes), about 42 MB at T = 16384, E = 384, d = 7168. */
 size_t siggate_workspace_bytes(const siggate_cfg_t *cfg);
 
 /* Gate.

@@ -60,6 +60,9 @@ def test_workspace_bytes():
     # slice), for the reduction that runs the selection
     x3 = dataclasses.replace(big, logits_path=1)
     assert sg.siggate_workspace_bytes(x3) >= 16384 * 256 * 4
+    # large batches: one slice of partial logits, then the three bf16 planes
+    kimi_big = dataclasses.replace(KIMI.with_T(16384), logits_path=1)
+    assert sg.siggate_workspace_bytes(kimi_big) == 16384 * 384 * 4 + 3 * 384 * 7168 * 2
     assert sg.siggate_workspace_bytes(dataclasses.replace(KIMI, logits_path=1)) >= 256 * 384 * 4
 
 
