@@ -103,3 +103,11 @@ def compare_dispatch(out, ref, indices: np.ndarray, x: np.ndarray, K: int,
         got = got.view(torch.int16).cpu().numpy().view(np.uint16)
         want = oracle.gather_rows(x, ref.perm, K, rows)
         assert np.array_equal(got, want), "permuted_x rows differ"
+
+
+def combine_tolerance(o, outs, w64, dest, y64, K):
+    """Bound on |GPU - float64 sum|: one bfloat16 unit of the result (the
+    final rounding) plus K float32 roundings of partial sums bounded by the
+    sum of absolute terms (computed by the oracle on |out| and |w|)."""
+    ya64, _ = o.combine(outs & np.uint16(0x7FFF), np.abs(w64), dest)
+    return 2.0 ** -7 * np.abs(y64) + K * 2.0 ** -23 * ya64 + 1e-38

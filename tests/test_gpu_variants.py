@@ -9,7 +9,7 @@ import pytest
 import oracle
 import sigmoid_group_limited_amd as sg
 from sigmoid_group_limited_amd import workloads as wl
-from parity import check_rows_valid, compare_gate, dev_inputs, say
+from parity import check_rows_valid, combine_tolerance, compare_gate, dev_inputs, say
 
 pytestmark = pytest.mark.gpu
 
@@ -80,14 +80,6 @@ def test_gate_variant(o, name, gc, T, d, opts, bias_kind, lp):
         if bias_kind == "negative":
             assert outside > 0, "the negative-bias case does not exercise the 0.0 fill"
     say(f"    {stats}")
-
-
-def combine_tolerance(o, outs, w64, dest, y64, K):
-    """Bound on |GPU - float64 sum|: one bfloat16 unit of the result (the
-    final rounding) plus K float32 roundings of partial sums bounded by the
-    sum of absolute terms (computed by the oracle on |out| and |w|)."""
-    ya64, _ = o.combine(outs & np.uint16(0x7FFF), np.abs(w64), dest)
-    return 2.0 ** -7 * np.abs(y64) + K * 2.0 ** -23 * ya64 + 1e-38
 
 
 def test_combine_parity(o):
