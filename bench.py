@@ -47,7 +47,9 @@ route's.
 ``cpu_baseline`` times the CPU oracle (float64, all host threads) on a
 bounded sample of the same workload, and reports how the GPU's result on
 those tokens compares with it (``gpu_parity``: tokens exempt for a score
-margin below 1e-6, non-exempt index mismatches, largest weight error).
+margin below 1e-6, non-exempt index mismatches, largest weight error, the
+largest error of the GPU's float32 choice scores, and the tokens whose
+margin lies between 1e-6 and twice that error).
 """
 from __future__ import annotations
 
@@ -365,6 +367,29 @@ def decode_line(name: str, calls: int = 20, replays: int = 5, logits_path: int =
             "graph_replay_matches_eager": bool(same)}
 
 
+def score_error(case: Case, o, n: int, margins: np.ndarray, same: np.ndarray) -> dict:
+    """How far the GPU's float32 choice scores v = sigmoid(L) + b can be
+    from the oracle's float64 ones on the first n tokens: the largest
+    |v32 - v64| over every token and expert, with v32 formed in float32 from
+    the GPU's own logits.  Tokens whose decision margin lies between the
+    1e-6 exemption threshold and twice that error are not exempt, yet the
+    score error alone could flip them: they are counted, with how many of
+    them differ from the oracle."""
+    c = case.cfg
+    lg = case.sg.siggate_logits(case.x[:n], case.W, c.with_T(n)).cpu().numpy()
+    lr = o.logits(case.gi.x[:n], case.gi.W)
+    one = np.float32(1.0)
+    s32 = one / (one + np.exp(-lg))          # float32 arithmetic
+    v32 = s32 + case.gi.bias.astype(np.float32)[None, :]
+    v64 = 1.0 / (1.0 + np.exp(-lr)) + case.gi.bias.astype(np.float64)[None, :]
+    err = float(np.abs(v32.astype(np.float64) - v64).max())
+    margin = np.minimum(margins[:, 0], margins[:, 1])
+    band = (margin >= 1e-6) & (margin < 2.0 * err)
+    return {"score_max_abs_err": err, "near_band": [1e-6, 2.0 * err],
+            "near_band_tokens": int(band.sum()),
+            "near_band_mismatch": int((band & ~same).sum())}
+
+
 def cpu_baseline(case: Case, budget_s: float = 12.0):
     """The oracle, as it stands, on the first n tokens of the workload: gate,
     then dispatch and row gather of those tokens' pairs.  n grows from 256
@@ -410,6 +435,7 @@ def cpu_baseline(case: Case, budget_s: float = 12.0):
               "exempt_matched": int((exempt & same).sum()),
               "index_mismatch_nonexempt": int((~same & ~exempt).sum()),
               "weight_max_rel": float(rel.max()) if rel.size else 0.0}
+    parity.update(score_error(case, o, n, r.margins, same))
     return dict(value=n / dt, unit="tokens/s", cores=o.num_threads(), kind="oracle",
                 gate_tokens_per_s=n / split["gate"],
                 dispatch_tokens_per_s=n / split["dispatch"],

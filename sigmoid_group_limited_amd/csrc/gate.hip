@@ -38,6 +38,7 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int KPAD = KC + 4;    // padded LDS row in floats: rows start 4 banks apart
 constexpr int SPLIT_STAGES = 4; // chunks of global loads in flight in the split GEMM
+constexpr int FLUSH_CHUNKS = 16; // chunks per float32 accumulation block
 
 // Workgroup of NW waves: 4 expert quarters x WM token splits x KS k-splits.
 // A k-split wave pair shares a tile and processes alternate halves of every
@@ -331,7 +332,12 @@ __device__ __forceinline__ void finish_tile(const GateArgs &a,
     }
 }
 
-template <int E, int MB, int NW, int MODE, int P>
+// BLOCKED: flush the accumulators into the totals every FLUSH_CHUNKS chunks
+// (long k ranges); without it only once, at the end (k-slices of at most
+// 2 * FLUSH_CHUNKS chunks, whose chains the slicing already keeps short --
+// the branch in the unrolled loop measurably slows those short tiles, and
+// long split tiles run it with P = 2, where it costs least).
+template <int E, int MB, int NW, int MODE, int P, bool BLOCKED>
 __global__ __launch_bounds__(64 * NW) void gate_gemm_kernel(GateArgs a)
 {
     using S = Shape<E, MB, NW>;
@@ -435,6 +441,37 @@ __global__ __launch_bounds__(64 * NW) void gate_gemm_kernel(GateArgs a)
     f32x16 acc2;
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc2[r] = 0.0f;
+    // Blocked summation: every FLUSH_CHUNKS chunks the accumulators are
+    // added into float32 totals and restarted from zero, so no rounding
+    // chain is longer than FLUSH_CHUNKS chunks (one chain over all of d=7168
+    // would be 3584 dependent additions).  Every wave flushes at the same
+    // chunks, so equal W rows still give bit-equal logits.  Short k-slices
+    // (not BLOCKED) add their accumulators into the totals once, at the end.
+    f32x16 tot[S::MBW][S::NB];
+#pragma unroll
+    for (int m = 0; m < S::MBW; ++m)
+#pragma unroll
+        for (int n = 0; n < S::NB; ++n)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) tot[m][n][r] = 0.0f;
+    auto flush = [&]() {
+#pragma unroll
+        for (int m = 0; m < S::MBW; ++m)
+#pragma unroll
+            for (int n = 0; n < S::NB; ++n)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    tot[m][n][r] += acc[m][n][r];
+                    acc[m][n][r] = 0.0f;
+                }
+        if constexpr (TWO_ACC) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                tot[0][0][r] += acc2[r];
+                acc2[r] = 0.0f;
+            }
+        }
+    };
 
     const int f_row = lane & 31;
     const int f_k = (lane >> 5) * 4;
@@ -475,8 +512,8 @@ __global__ __launch_bounds__(64 * NW) void gate_gemm_kernel(GateArgs a)
     // After the first 8-column group of chunk c, chunk c+1 is written to the
     // other LDS buffer and its register stage is refilled with chunk c+1+P,
     // so every global load has P chunks of MFMA work to land in (P = 2 for
-    // the long fused tiles; more for the short split tiles, whose chunks are
-    // a sixth as long).  The one barrier per chunk comes once the last
+    // the long fused tiles and long k-slices; 4 for the short split tiles,
+    // whose chunks are a sixth as long).  The one barrier per chunk comes once the last
     // fragments of chunk c are in registers: the MFMAs of that last group
     // then cover the LDS latency of the first fragments of chunk c+1.  Local
     // chunk i uses LDS buffer i%2 and stage (i+1)%P, so the loop is unrolled
@@ -577,10 +614,14 @@ __global__ __launch_bounds__(64 * NW) void gate_gemm_kernel(GateArgs a)
         __syncthreads();
         read_frag(0, g0, f);
         constexpr int U = P % 2 ? 2 * P : P;
+        static_assert(FLUSH_CHUNKS % U == 0, "flushes fall between unrolled steps");
         int c = c_begin;
         for (; c + U <= c_end; c += U) {
 #pragma unroll
             for (int u = 0; u < U; ++u) step(c + u, u & 1, st[(u + 1) % P]);
+            if constexpr (BLOCKED) {
+                if ((c + U - c_begin) % FLUSH_CHUNKS == 0) flush();
+            }
         }
 #pragma unroll
         for (int u = 0; u < U - 1; ++u)
@@ -588,10 +629,11 @@ __global__ __launch_bounds__(64 * NW) void gate_gemm_kernel(GateArgs a)
         __syncthreads();   // every wave is done with the staging buffers
     }
 
-    if constexpr (TWO_ACC) {
+    flush();
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[0][0][r] += acc2[r];
-    }
+    for (int m = 0; m < S::MBW; ++m)
+#pragma unroll
+        for (int n = 0; n < S::NB; ++n) acc[m][n] = tot[m][n];
 
     if constexpr (S::KS == 2) {
         // k-split pair: the second wave hands its sums to the first, which
@@ -745,17 +787,23 @@ hipError_t launch_for_e(const GateArgs &a, const GatePlan &p, GateMode final_mod
         // pair split every chunk's k
         const dim3 grid(p.grid), block(64 * 8);
         if (p.m_blocks == 2)
-            return sel ? launch_kernel(gate_gemm_kernel<E, 2, 8, MODE_SELECT, 2>, grid, block, stream, a)
-                       : launch_kernel(gate_gemm_kernel<E, 2, 8, MODE_LOGITS, 2>, grid, block, stream, a);
-        return sel ? launch_kernel(gate_gemm_kernel<E, 1, 8, MODE_SELECT, 2>, grid, block, stream, a)
-                   : launch_kernel(gate_gemm_kernel<E, 1, 8, MODE_LOGITS, 2>, grid, block, stream, a);
+            return sel ? launch_kernel(gate_gemm_kernel<E, 2, 8, MODE_SELECT, 2, true>, grid, block, stream, a)
+                       : launch_kernel(gate_gemm_kernel<E, 2, 8, MODE_LOGITS, 2, true>, grid, block, stream, a);
+        return sel ? launch_kernel(gate_gemm_kernel<E, 1, 8, MODE_SELECT, 2, true>, grid, block, stream, a)
+                   : launch_kernel(gate_gemm_kernel<E, 1, 8, MODE_LOGITS, 2, true>, grid, block, stream, a);
     }
     // split GEMM: 32 tokens x 128 experts, 8 waves (two per SIMD): 4 columns
     // of 32 experts x 2 k-halves of every chunk; or the bfloat16 three-way
     // route, which writes the same partials
-    hipError_t e = p.x3_bm ? launch_x3_gemm(a, p, stream)
-                           : launch_kernel(gate_gemm_kernel<128, 1, 8, MODE_PARTIAL, SPLIT_STAGES>,
-                                           dim3(p.grid), dim3(64 * 8), stream, a);
+    hipError_t e;
+    if (p.x3_bm)
+        e = launch_x3_gemm(a, p, stream);
+    else if (p.chunks_per_split > 2 * FLUSH_CHUNKS)   // long k-slices: blocked, 2 stages
+        e = launch_kernel(gate_gemm_kernel<128, 1, 8, MODE_PARTIAL, 2, true>,
+                          dim3(p.grid), dim3(64 * 8), stream, a);
+    else
+        e = launch_kernel(gate_gemm_kernel<128, 1, 8, MODE_PARTIAL, SPLIT_STAGES, false>,
+                          dim3(p.grid), dim3(64 * 8), stream, a);
     if (e != hipSuccess) return e;
     // few slices: one wave per token loads them all at once; more: 16 waves
     // per token, each loading a contiguous run of them

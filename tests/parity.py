@@ -111,3 +111,21 @@ def combine_tolerance(o, outs, w64, dest, y64, K):
     sum of absolute terms (computed by the oracle on |out| and |w|)."""
     ya64, _ = o.combine(outs & np.uint16(0x7FFF), np.abs(w64), dest)
     return 2.0 ** -7 * np.abs(y64) + K * 2.0 ** -23 * ya64 + 1e-38
+
+
+def score_error(lg_gpu: np.ndarray, lg_ref: np.ndarray, bias: np.ndarray,
+                margins: np.ndarray, same: np.ndarray) -> dict:
+    """Largest |v32 - v64| of the sigmoid choice scores v = sigmoid(L) + b,
+    v32 formed in float32 from the GPU's logits and v64 in float64 from the
+    oracle's, over every token and expert given; and the tokens whose margin
+    lies between the exemption threshold and twice that error (not exempt,
+    yet within reach of the score error), with how many differ."""
+    one = np.float32(1.0)
+    v32 = one / (one + np.exp(-lg_gpu.astype(np.float32))) + bias.astype(np.float32)[None, :]
+    v64 = 1.0 / (1.0 + np.exp(-lg_ref)) + bias.astype(np.float64)[None, :]
+    err = float(np.abs(v32.astype(np.float64) - v64).max())
+    margin = np.minimum(margins[:, 0], margins[:, 1])
+    band = (margin >= EXEMPT_MARGIN) & (margin < 2.0 * err)
+    return {"score_max_abs_err": err, "near_band_tokens": int(band.sum()),
+            "near_band_mismatch": int((band & ~same).sum())}
+

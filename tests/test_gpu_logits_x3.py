@@ -16,7 +16,8 @@ import pytest
 import oracle
 import sigmoid_group_limited_amd as sg
 from sigmoid_group_limited_amd import workloads as wl
-from parity import LOGIT_RTOL, check_rows_valid, compare_dispatch, compare_gate, dev_inputs, say
+from parity import (LOGIT_RTOL, check_rows_valid, compare_dispatch, compare_gate, dev_inputs, say,
+                    score_error)
 
 pytestmark = pytest.mark.gpu
 
@@ -186,6 +187,11 @@ def test_x3_workload_full_size(o, name):
         np.unique(np.r_[0, 1, w.T - 1, rng.integers(0, w.T, 768)])
     ref = oracle_gate(o, gi, cfg, rows)
     stats = compare_gate(w_np, i_np, ref, w.cfg.route_scale, rows)
+    lg = sg.siggate_logits(x, W, cfg).cpu().numpy()[rows]
+    stats.update(score_error(lg, o.logits(gi.x[rows], gi.W), gi.bias, ref.margins,
+                             np.all(i_np[rows] == ref.indices, axis=1)))
+    # measured 1.1-1.3e-6 on this route's full-size batches
+    assert stats["score_max_abs_err"] < 2e-6, stats
     if gi.twins:
         dec = np.zeros(len(rows), bool)
         for a, bb in gi.twins:

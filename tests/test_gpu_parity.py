@@ -12,7 +12,7 @@ import oracle
 import sigmoid_group_limited_amd as sg
 from sigmoid_group_limited_amd import workloads as wl
 from parity import (LOGIT_RTOL, check_rows_valid, compare_dispatch, compare_gate,
-                    dev_inputs, say)
+                    dev_inputs, say, score_error)
 
 pytestmark = pytest.mark.gpu
 
@@ -31,6 +31,10 @@ def gpu():
     sg.load_library()
     yield
     torch.cuda.synchronize()
+
+
+# largest |v32 - v64| of the choice scores allowed on the float32 route
+SCORE_ERR_MAX = 1e-6
 
 
 def cfg_of(gc: wl.GateConfig, T: int, d: int, order: int = 0) -> sg.Cfg:
@@ -128,7 +132,12 @@ def test_gate_plan_sweep(o, T, E):
     rows = np.arange(T) if T <= 300 else np.unique(np.r_[0, 31, 32, T - 1, rng.integers(0, T, 200)])
     ref = oracle_gate(o, gi, cfg, rows)
     stats = compare_gate(w, i, ref, gc.route_scale, rows)
+    x, W, _ = dev_inputs(gi)
+    lg = sg.siggate_logits(x, W, cfg).cpu().numpy()[rows]
+    stats.update(score_error(lg, o.logits(gi.x[rows], gi.W), gi.bias, ref.margins,
+                             np.all(i[rows] == ref.indices, axis=1)))
     say(f"    {stats}")
+    assert stats["score_max_abs_err"] < SCORE_ERR_MAX, stats
 
 
 @pytest.mark.parametrize("T,E,d", [(100, 256, 7168), (16384, 384, 96), (9000, 128, 40)])
@@ -184,6 +193,13 @@ def test_workload_full_size(o, name):
         np.unique(np.r_[0, 1, w.T - 1, rng.integers(0, w.T, 768)])
     ref = oracle_gate(o, gi, cfg, rows)
     stats = compare_gate(w_np, i_np, ref, w.cfg.route_scale, rows)
+    lg = sg.siggate_logits(x, W, cfg).cpu().numpy()[rows]
+    stats.update(score_error(lg, o.logits(gi.x[rows], gi.W), gi.bias, ref.margins,
+                             np.all(i_np[rows] == ref.indices, axis=1)))
+    # the exemption margin must stay above the float32 score error (one
+    # accumulation chain over all of d measured 2.1-2.8e-6 here; blocked
+    # summation 5e-7)
+    assert stats["score_max_abs_err"] < SCORE_ERR_MAX, stats
     if gi.twins:
         dec = np.zeros(len(rows), bool)
         for a, bb in gi.twins:
