@@ -187,9 +187,17 @@ def test_x3_workload_full_size(o, name):
         np.unique(np.r_[0, 1, w.T - 1, rng.integers(0, w.T, 768)])
     ref = oracle_gate(o, gi, cfg, rows)
     stats = compare_gate(w_np, i_np, ref, w.cfg.route_scale, rows)
-    lg = sg.siggate_logits(x, W, cfg).cpu().numpy()[rows]
+    lg_all = sg.siggate_logits(x, W, cfg).cpu().numpy()
+    lg = lg_all[rows]
     stats.update(score_error(lg, o.logits(gi.x[rows], gi.W), gi.bias, ref.margins,
                              np.all(i_np[rows] == ref.indices, axis=1)))
+    # every token: the oracle's selection on the GPU's own logits (the
+    # selection epilogue apart from the GEMM's rounding), same rules
+    sel = o.select(lg_all.astype(np.float64), gi.bias, w.cfg.n_group, w.cfg.topk_group,
+                   w.cfg.top_k, w.cfg.route_scale)
+    s_all = compare_gate(w_np, i_np, sel, w.cfg.route_scale)
+    stats["select_on_gpu_logits"] = {k: s_all[k] for k in ("tokens", "exempt", "index_mismatch_nonexempt",
+                                                           "weight_max_rel")}
     # measured 1.1-1.3e-6 on this route's full-size batches
     assert stats["score_max_abs_err"] < 2e-6, stats
     if gi.twins:

@@ -193,9 +193,17 @@ def test_workload_full_size(o, name):
         np.unique(np.r_[0, 1, w.T - 1, rng.integers(0, w.T, 768)])
     ref = oracle_gate(o, gi, cfg, rows)
     stats = compare_gate(w_np, i_np, ref, w.cfg.route_scale, rows)
-    lg = sg.siggate_logits(x, W, cfg).cpu().numpy()[rows]
+    lg_all = sg.siggate_logits(x, W, cfg).cpu().numpy()
+    lg = lg_all[rows]
     stats.update(score_error(lg, o.logits(gi.x[rows], gi.W), gi.bias, ref.margins,
                              np.all(i_np[rows] == ref.indices, axis=1)))
+    # every token: the oracle's selection on the GPU's own logits (the
+    # selection epilogue apart from the GEMM's rounding), same rules
+    sel = o.select(lg_all.astype(np.float64), gi.bias, w.cfg.n_group, w.cfg.topk_group,
+                   w.cfg.top_k, w.cfg.route_scale)
+    s_all = compare_gate(w_np, i_np, sel, w.cfg.route_scale)
+    stats["select_on_gpu_logits"] = {k: s_all[k] for k in ("tokens", "exempt", "index_mismatch_nonexempt",
+                                                           "weight_max_rel")}
     # the exemption margin must stay above the float32 score error (one
     # accumulation chain over all of d measured 2.1-2.8e-6 here; blocked
     # summation 5e-7)
