@@ -204,6 +204,8 @@ __global__ __launch_bounds__(256) void dispatch_gather_kernel(DispatchArgs a)
 // come from integer atomics, so the result does not depend on their order.
 constexpr int SMALL_PAIRS = 4096;
 constexpr int SMALL_NT = 256;
+constexpr int SMALL_PF = 4;   // row pieces per thread loaded before the count
+constexpr int SMALL_CB = 8;   // index loads per thread issued together in the count
 
 __global__ __launch_bounds__(SMALL_NT) void dispatch_small_kernel(DispatchArgs a, int parts)
 {
@@ -218,13 +220,36 @@ __global__ __launch_bounds__(SMALL_NT) void dispatch_small_kernel(DispatchArgs a
     const int K = a.top_k;
     const int first = t * K;              // pairs of tokens before t
     const int npairs = a.T * K;
+    // this block's slice [v0, v1) of row t, in 16-byte pieces; the first
+    // SMALL_PF pieces of each thread are loaded now, so that their latency
+    // overlaps the count below
+    const int nvec = a.d / 8;
+    const int per = (nvec + parts - 1) / parts;
+    const int v0 = part * per;
+    const int v1 = min(nvec, v0 + per);
+    const u32x4 *src = (const u32x4 *)(a.x + (size_t)t * a.d);
+    u32x4 pf[SMALL_PF] = {};
+#pragma unroll
+    for (int j = 0; j < SMALL_PF; ++j) {
+        const int i = v0 + tid + j * SMALL_NT;
+        if (i < v1) pf[j] = src[i];
+    }
     for (int x = tid; x < a.E; x += SMALL_NT) cnt[x] = before[x] = 0;
     __syncthreads();
-    for (int p = tid; p < npairs; p += SMALL_NT) {
-        const int e = a.indices[p];
-        if ((unsigned)e < (unsigned)a.E) {
-            atomicAdd(&cnt[e], 1);
-            if (p < first) atomicAdd(&before[e], 1);
+    // SMALL_CB index loads in flight before their atomics
+    for (int p0 = 0; p0 < npairs; p0 += SMALL_CB * SMALL_NT) {
+        int e[SMALL_CB];
+#pragma unroll
+        for (int j = 0; j < SMALL_CB; ++j) {
+            const int p = p0 + j * SMALL_NT + tid;
+            e[j] = p < npairs ? a.indices[p] : -1;
+        }
+#pragma unroll
+        for (int j = 0; j < SMALL_CB; ++j) {
+            if ((unsigned)e[j] < (unsigned)a.E) {
+                atomicAdd(&cnt[e[j]], 1);
+                if (p0 + j * SMALL_NT + tid < first) atomicAdd(&before[e[j]], 1);
+            }
         }
     }
     __syncthreads();
@@ -270,11 +295,17 @@ __global__ __launch_bounds__(SMALL_NT) void dispatch_small_kernel(DispatchArgs a
     int dst[MAX_TOPK];
 #pragma unroll
     for (int k = 0; k < MAX_TOPK; ++k) dst[k] = k < K ? pos_s[k] : -1;
-    const int nvec = a.d / 8;
-    const int per = (nvec + parts - 1) / parts;
-    const int v1 = min(nvec, (part + 1) * per);
-    const u32x4 *src = (const u32x4 *)(a.x + (size_t)t * a.d);
-    for (int i = part * per + tid; i < v1; i += SMALL_NT) {
+#pragma unroll
+    for (int j = 0; j < SMALL_PF; ++j) {
+        const int i = v0 + tid + j * SMALL_NT;
+        if (i < v1) {
+#pragma unroll
+            for (int k = 0; k < MAX_TOPK; ++k)
+                if (dst[k] >= 0)
+                    __builtin_nontemporal_store(pf[j], (u32x4 *)(a.permuted_x + (size_t)dst[k] * a.d) + i);
+        }
+    }
+    for (int i = v0 + tid + SMALL_PF * SMALL_NT; i < v1; i += SMALL_NT) {
         const u32x4 val = src[i];
 #pragma unroll
         for (int k = 0; k < MAX_TOPK; ++k)
