@@ -31,6 +31,10 @@ and the HBM time (MFMA binds at both sizes).
 each option of the configuration: softmax scoring, no bias (group maximum),
 and the 0.0 fill with the 1e-20 denominator epsilon, beside the default.
 
+``skewed`` is the DeepSeek-V3 batch of T=65536 tokens whose 16 hot experts
+(two per group) draw half of the 524288 pairs: whole steps as for the main
+workload, with the share of pairs that went to the hot experts.
+
 ``overlap`` runs independent batches of the workload with the gates on one
 HIP stream and the dispatches on another (two batches in flight), so that
 one batch's HBM-bound dispatch overlaps the next batch's MFMA-bound gate; it
@@ -367,6 +371,29 @@ def decode_line(name: str, calls: int = 20, replays: int = 5, logits_path: int =
             "graph_replay_matches_eager": bool(same)}
 
 
+def skewed_line(logits_path: int, steps: int, warmup: int) -> dict:
+    """The skewed DeepSeek-V3 batch: T=65536 with 16 hot experts (two per
+    group) that draw half of the 524288 pairs.  Whole steps as for the main
+    workload, against the path roofline t_gate + t_dispatch."""
+    case = Case("dsv3-skewed", logits_path)
+    ms, gate_ms, disp_ms = case.run(steps, warmup)
+    flops, _, disp_bytes = case.algorithmic()
+    T = case.w.T
+    mfma_flops = flops if logits_path == 0 else 3 * flops
+    peak = PEAK_FP32_MFMA_TFLOPS if logits_path == 0 else PEAK_BF16_MFMA_TFLOPS
+    t_roof = mfma_flops / (peak * 1e12) + disp_bytes / (PEAK_HBM_GBS * 1e9)
+    hot = float(np.isin(case.indices.cpu().numpy(), case.gi.hot).mean())
+    out = {"workload": case.w.name, "T": T, "E": case.cfg.E, "logits_path": logits_path,
+           "value": T / (ms * 1e-3), "unit": "tokens/s", "ms_per_step": ms,
+           "gate_ms": gate_ms, "dispatch_ms": disp_ms,
+           "gate_mfma_frac": mfma_flops / (gate_ms * 1e-3) / 1e12 / peak,
+           "dispatch_algorithmic_GBps": disp_bytes / (disp_ms * 1e-3) / 1e9,
+           "roofline_tokens_per_s": T / t_roof, "path_roofline_frac": t_roof / (ms * 1e-3),
+           "hot_share": hot}
+    del case
+    return out
+
+
 def score_error(case: Case, o, n: int, margins: np.ndarray, same: np.ndarray) -> dict:
     """How far the GPU's float32 choice scores v = sigmoid(L) + b can be
     from the oracle's float64 ones on the first n tokens: the largest
@@ -455,6 +482,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true",
                     help="skip the graph-replayed decode-size lines")
     ap.add_argument("--no-cold", action="store_true", help="skip the scrubbed (cold) steps")
+    ap.add_argument("--no-skewed", action="store_true",
+                    help="skip the skewed DeepSeek-V3 batch (T=65536, hot experts)")
     ap.add_argument("--no-overlap", action="store_true",
                     help="skip the two-stream run of two independent batches")
     ap.add_argument("--no-bf16x3", action="store_true",
@@ -549,6 +578,8 @@ def main():
             "variants": sec.run_variants(max(5, args.steps // 2), 2),
         }
         del sec
+    if not args.no_skewed:
+        result["skewed"] = skewed_line(lp, max(5, args.steps // 2), 2)
     if not args.no_overlap:
         result["overlap"] = overlap_line(args.workload, max(8, args.steps), 2)
     if not args.no_decode:
