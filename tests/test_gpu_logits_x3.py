@@ -109,7 +109,7 @@ def test_x3_plan_sweep(o, T, E):
 
 
 @pytest.mark.parametrize("T,E,d", [(100, 256, 7168), (16384, 384, 96), (9000, 128, 40),
-                                   (300, 384, 264)])
+                                   (300, 384, 264), (16384, 384, 7168), (2048, 256, 7168)])
 def test_x3_logits_exact_on_integer_inputs(o, T, E, d):
     """x small integers, W integers times 2^-8: every partial sum is exact,
     so the logits equal the oracle's bit for bit."""

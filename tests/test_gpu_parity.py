@@ -140,11 +140,16 @@ def test_gate_plan_sweep(o, T, E):
     assert stats["score_max_abs_err"] < SCORE_ERR_MAX, stats
 
 
-@pytest.mark.parametrize("T,E,d", [(100, 256, 7168), (16384, 384, 96), (9000, 128, 40)])
+@pytest.mark.parametrize("T,E,d", [
+    (100, 256, 7168), (16384, 384, 96), (9000, 128, 40),
+    # full d with blocked summation: fused 64- and 32-token tiles flushing
+    # every 16 chunks, and split tiles with long k-slices (1 and 5 slices)
+    (16384, 384, 7168), (9000, 256, 7168), (4096, 256, 7168), (512, 384, 7168)])
 def test_logits_exact_on_integer_inputs(o, T, E, d):
     """x small integers, W integers times 2^-8: every partial sum is exact in
     float32, so GPU logits equal the oracle's bit for bit on both the split
-    and the fused paths."""
+    and the fused paths, whatever the blocking of the sums (a flush that
+    dropped or repeated a chunk would show here)."""
     say(f"[logits-exact] T={T} E={E} d={d}")
     rng = np.random.default_rng(T)
     xi = rng.integers(-8, 9, size=(T, d)).astype(np.float32)
