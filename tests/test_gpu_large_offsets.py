@@ -15,6 +15,7 @@ or the copied bytes, which the comparisons below catch.
 Checks:
   * the gate on both logits routes, sampled rows against the oracle (rows
     past the boundary among them), and the row properties on every token;
+  * every repeat of a block row gets bit-equal weights and indices;
   * the dispatch in full: counts, offsets, perm and dest;
   * the permuted rows and the combined output at sampled positions past
     2^32 bytes, against the oracle."""
@@ -78,6 +79,11 @@ def test_offsets_past_32_bits(o):
         torch.cuda.synchronize()
         w_np, i_np = w.cpu().numpy(), i.cpu().numpy()
         check_rows_valid(i_np, E, gc.n_group, gc.topk_group)
+        # equal rows of x give bit-equal results wherever they sit in the
+        # batch (every row's sums run in the same order)
+        same_row = np.arange(T) % R
+        assert np.array_equal(i_np, i_np[same_row]) and np.array_equal(w_np, w_np[same_row]), \
+            "repeated rows of x were routed differently"
         stats = compare_gate(w_np, i_np, ref, gc.route_scale, rows)
         say(f"    gate logits_path={lp}: {stats}")
         if lp == 0:
