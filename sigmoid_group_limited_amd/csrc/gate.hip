@@ -826,6 +826,9 @@ hipError_t launch_for_e(const GateArgs &a, const GatePlan &p, GateMode final_mod
 constexpr double SPLIT_LATENCY = 4.0;
 constexpr double SPLIT_BYTES_PER_UNIT = 2.25e6;
 constexpr int N_CU = 256;
+// time of a round of 64-token fused workgroups over a round of 32-token ones
+// (measured 1.72 at E=384, 1.77 at E=256, d=7168)
+constexpr double FUSED_ROUND_RATIO = 1.75;
 
 GatePlan plan_gate(int T, int d, int E, int path)
 {
@@ -839,8 +842,12 @@ GatePlan plan_gate(int T, int d, int E, int path)
     p.e_tiles = 1;
     // Enough 64- or 32-token workgroups for every compute unit: one
     // workgroup per token tile, all experts, whole k range, fused selection.
+    // The tile height goes by whole rounds of N_CU workgroups: a round of
+    // 64-token tiles takes about FUSED_ROUND_RATIO times a round of 32-token
+    // ones, and a partly filled last round costs a whole one.
     if (tiles64 >= N_CU || tiles32 >= N_CU) {
-        p.m_blocks = tiles64 >= N_CU ? 2 : 1;
+        const long r64 = (tiles64 + N_CU - 1) / N_CU, r32 = (tiles32 + N_CU - 1) / N_CU;
+        p.m_blocks = (double)r64 * FUSED_ROUND_RATIO < (double)r32 ? 2 : 1;
         p.t_tiles = (int)(p.m_blocks == 2 ? tiles64 : tiles32);
         p.grid = p.t_tiles;
         return p;

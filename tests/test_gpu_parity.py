@@ -64,16 +64,22 @@ SMALL = [
     ("e256_g1_k1_T50", wl.GateConfig(256, 1, 1, 1, 1.0), 50, 7168),
     ("e384_g2_T129_d264", wl.GateConfig(384, 2, 1, 8, 2.827), 129, 264),
     ("e256_g8_k3_T4100_d256", wl.GateConfig(256, 8, 4, 3, 2.5), 4100, 256),
-    # fused (single k-slice) paths: 32-token and 64-token workgroups, ragged tails
-    ("dsv3_fused32_T8229_d256", wl.DSV3, 8229, 256),
-    ("kimi_fused64_T16389_d256", wl.KIMI_K2, 16389, 256),
-    ("dsv3_fused64_T16447_d200", wl.DSV3, 16447, 200),
-    ("e128_g4_fused64_T16400_d96", wl.GateConfig(128, 4, 2, 6, 1.0), 16400, 96),
+    # fused (single k-slice) paths: 32-token and 64-token workgroups, ragged
+    # tails; the tile height goes by whole rounds of 256 workgroups, so
+    # 8180 and 16389-24576 tokens take 32-token tiles, 8229-16384 and
+    # 24577-32768 take 64-token ones (a partly filled round among them)
+    ("dsv3_fused32_T8180_d256", wl.DSV3, 8180, 256),
+    ("dsv3_fused64_partial_round_T8229_d256", wl.DSV3, 8229, 256),
+    ("kimi_fused32_T16389_d256", wl.KIMI_K2, 16389, 256),
+    ("kimi_fused64_T16380_d256", wl.KIMI_K2, 16380, 256),
+    ("dsv3_fused64_T16350_d200", wl.DSV3, 16350, 200),
+    ("e128_g4_fused64_T16321_d96", wl.GateConfig(128, 4, 2, 6, 1.0), 16321, 96),
+    ("dsv3_fused64_two_rounds_T24600_d136", wl.DSV3, 24600, 136),
     # degenerate: the kept groups hold exactly top_k experts (all of them win)
     ("e128_g64_kg4_k8_all_kept_T300_d512", wl.GateConfig(128, 64, 4, 8, 1.0), 300, 512),
     # every group kept (the group stage selects nothing away)
     ("e256_g8_kg8_T200_d1024", wl.GateConfig(256, 8, 8, 8, 2.5), 200, 1024),
-    ("e128_g1_fused32_T9000_d136", wl.GateConfig(128, 1, 1, 8, 2.5), 9000, 136),
+    ("e128_g1_fused32_T20000_d136", wl.GateConfig(128, 1, 1, 8, 2.5), 20000, 136),
 ]
 
 
@@ -114,7 +120,8 @@ def test_gate_parity_small(o, name, gc, T, d, order):
 # down to 1 (expert tiles only), 4 and 16 reduction waves, grids padded to a
 # multiple of 8, ragged last token tiles; and both fused tile heights.
 PLAN_SWEEP = [(2, 256), (33, 384), (65, 256), (129, 384), (300, 256), (511, 384),
-              (1000, 256), (2047, 384), (4000, 256), (6000, 384), (8191, 256), (12000, 384)]
+              (1000, 256), (2047, 384), (4000, 256), (6000, 384), (8191, 256), (12000, 384),
+              (20000, 384)]
 
 
 @pytest.mark.parametrize("T,E", PLAN_SWEEP, ids=[f"T{t}_E{e}" for t, e in PLAN_SWEEP])
@@ -144,7 +151,7 @@ def test_gate_plan_sweep(o, T, E):
     (100, 256, 7168), (16384, 384, 96), (9000, 128, 40),
     # full d with blocked summation: fused 64- and 32-token tiles flushing
     # every 16 chunks, and split tiles with long k-slices (1 and 5 slices)
-    (16384, 384, 7168), (9000, 256, 7168), (4096, 256, 7168), (512, 384, 7168)])
+    (16384, 384, 7168), (20480, 256, 7168), (4096, 256, 7168), (512, 384, 7168)])
 def test_logits_exact_on_integer_inputs(o, T, E, d):
     """x small integers, W integers times 2^-8: every partial sum is exact in
     float32, so GPU logits equal the oracle's bit for bit on both the split
