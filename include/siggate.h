@@ -83,7 +83,8 @@ typedef struct siggate_cfg {
      *   1 = each float32 weight split exactly into three bfloat16 parts
      *       (W = hi + mid + lo), x * each part (exact products) added into
      *       float32 accumulators on the bfloat16 matrix cores
-     *       (v_mfma_f32_16x16x32_bf16).  Exact split for |W| >= 2^-110;
+     *       (v_mfma_f32_16x16x32_bf16).  Every part is a normal number
+     *       for |W| >= 2^-103 (smaller W may give subnormal parts);
      *       the logits differ from route 0 by float32 summation order only.
      * Accuracy on N(0,1)-sized logits at d = 7168: route 0 adds its
      * accumulators into float32 totals every 512 columns (blocked

@@ -54,10 +54,18 @@ def _needs_build(output: str, source: str) -> bool:
 
 
 @dataclass
+class Scores:
+    affinity: np.ndarray  # float64 [T, E]: s (sigmoid or softmax of the logits)
+    choice: np.ndarray    # float64 [T, E]: v = s + bias (v = s without a bias)
+    group: np.ndarray     # float64 [T, G]: group scores (empty when G == 1)
+
+
+@dataclass
 class GateResult:
     weights: np.ndarray   # float64 [T, K]
     indices: np.ndarray   # int32   [T, K]
     margins: np.ndarray   # float64 [T, 2]: (v_K - v_K+1, gs_KG - gs_KG+1)
+    scores: Scores | None = None   # the float64 scores the selection ranked
 
 
 @dataclass
@@ -88,6 +96,9 @@ class Oracle:
         lib.oracle_select.argtypes = [P(dbl), P(ctypes.c_float), i64, i64,
                                       i32, i32, i32, dbl, i32, i32, i32, i32,
                                       dbl, P(dbl), P(ctypes.c_int32), P(dbl)]
+        lib.oracle_scores.restype = i32
+        lib.oracle_scores.argtypes = [P(dbl), P(ctypes.c_float), i64, i64, i32, i32,
+                                      P(dbl), P(dbl), P(dbl)]
         lib.oracle_gate.restype = i32
         lib.oracle_gate.argtypes = [P(ctypes.c_uint16), P(ctypes.c_float),
                                     P(ctypes.c_float), i64, i64, i64, i32,
@@ -146,11 +157,13 @@ class Oracle:
     def select(self, logits: np.ndarray, bias: np.ndarray | None, n_group: int,
                topk_group: int, top_k: int, route_scale: float,
                order: int = 0, score_func: int = 0, renorm: int = 0,
-               mask_zero: int = 0, denom_eps: float = 0.0) -> GateResult:
+               mask_zero: int = 0, denom_eps: float = 0.0,
+               with_scores: bool = False) -> GateResult:
         """Gate steps after the logits, from float64 logits [T, E].
         bias=None selects the no-bias variant (group score = group max);
         score_func 0 sigmoid / 1 softmax; renorm 0 auto / 1 on / 2 off;
-        mask_zero fills dropped groups with 0.0 instead of -inf."""
+        mask_zero fills dropped groups with 0.0 instead of -inf.
+        with_scores also returns the float64 scores that were ranked."""
         L = np.ascontiguousarray(logits, dtype=np.float64)
         T, E = L.shape
         b, bp = self._bias_ptr(bias, E)
@@ -166,12 +179,32 @@ class Oracle:
                                     _ptr(m, ctypes.c_double))
         if rc != OK:
             raise ValueError(f"oracle_select rejected the configuration (rc={rc})")
-        return GateResult(w, idx, m)
+        sc = self.scores(L, bias, n_group, score_func) if with_scores else None
+        return GateResult(w, idx, m, sc)
+
+    def scores(self, logits: np.ndarray, bias: np.ndarray | None, n_group: int,
+               score_func: int = 0) -> Scores:
+        """Affinities, choice scores and group scores (steps 2-4) from
+        float64 logits [T, E]; the same code the selection runs."""
+        L = np.ascontiguousarray(logits, dtype=np.float64)
+        T, E = L.shape
+        b, bp = self._bias_ptr(bias, E)
+        s = np.empty((T, E), dtype=np.float64)
+        v = np.empty((T, E), dtype=np.float64)
+        G = n_group
+        gs = np.empty((T, G if G > 1 else 0), dtype=np.float64)
+        gsp = _ptr(gs, ctypes.c_double) if G > 1 else ctypes.POINTER(ctypes.c_double)()
+        rc = self.lib.oracle_scores(_ptr(L, ctypes.c_double), bp, T, E, G, score_func,
+                                    _ptr(s, ctypes.c_double), _ptr(v, ctypes.c_double), gsp)
+        if rc != OK:
+            raise ValueError(f"oracle_scores rejected the configuration (rc={rc})")
+        return Scores(s, v, gs)
 
     def gate(self, x_bf16: np.ndarray, W: np.ndarray, bias: np.ndarray | None,
              n_group: int, topk_group: int, top_k: int, route_scale: float,
              order: int = 0, score_func: int = 0, renorm: int = 0,
-             mask_zero: int = 0, denom_eps: float = 0.0) -> GateResult:
+             mask_zero: int = 0, denom_eps: float = 0.0,
+             with_scores: bool = False) -> GateResult:
         """Whole gate from bfloat16 bits x [T, d], float32 W [E, d], bias [E]
         (or None); options as in select()."""
         x = np.ascontiguousarray(x_bf16, dtype=np.uint16)
@@ -193,7 +226,8 @@ class Oracle:
                                   _ptr(m, ctypes.c_double))
         if rc != OK:
             raise ValueError(f"oracle_gate rejected the configuration (rc={rc})")
-        return GateResult(w, idx, m)
+        sc = self.scores(self.logits(x, W), bias, n_group, score_func) if with_scores else None
+        return GateResult(w, idx, m, sc)
 
     def dispatch(self, indices: np.ndarray, n_experts: int) -> DispatchResult:
         """Counts, offsets and the stable expert-major permutation."""

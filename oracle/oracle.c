@@ -135,19 +135,12 @@ typedef struct {
     double denom_eps;  /* added to the renormalisation denominator         */
 } gate_opts;
 
-/* Steps 2-8 for one token, from its E logits.
+/* Steps 2-4 for one token, from its E logits: affinities s, choice scores
+ * v and (when G > 1) group scores gs.
  *   bias: [E] or NULL (no bias: choice score = affinity, group score =
- *         group maximum)
- *   scratch: s, v, mv of E doubles; keep, gs of G; chosen of E; sel of K
- *   out_w[K], out_i[K]: weights and expert ids
- *   margin[2]: {K-th minus (K+1)-th masked choice score,
- *               KG-th minus (KG+1)-th group score}; +inf when undefined. */
-static void select_token(const double *L, const float *bias, int64_t E, int G,
-                         int KG, int K, double route_scale, int order,
-                         const gate_opts *opt, double *s, double *v,
-                         double *mv, int *keep, double *gs, int *chosen,
-                         int64_t *sel, double *out_w, int32_t *out_i,
-                         double *margin)
+ *         group maximum) */
+static void token_scores(const double *L, const float *bias, int64_t E, int G,
+                         const gate_opts *opt, double *s, double *v, double *gs)
 {
     const int64_t S = E / G;
 
@@ -166,9 +159,7 @@ static void select_token(const double *L, const float *bias, int64_t E, int G,
     /* Step 3: the bias shifts the choice score only. */
     for (int64_t e = 0; e < E; ++e) v[e] = s[e] + (bias ? (double)bias[e] : 0.0);
 
-    /* Steps 4-5: group scores and group keep mask. */
-    for (int g = 0; g < G; ++g) keep[g] = 1;
-    margin[1] = INFINITY;
+    /* Step 4: group scores. */
     if (G > 1) {
         for (int g = 0; g < G; ++g) {
             /* two largest values of the group, counting multiplicity */
@@ -186,6 +177,32 @@ static void select_token(const double *L, const float *bias, int64_t E, int G,
             else
                 gs[g] = top1;   /* no bias: the group maximum */
         }
+    }
+}
+
+/* Steps 2-8 for one token, from its E logits.
+ *   bias: [E] or NULL (no bias: choice score = affinity, group score =
+ *         group maximum)
+ *   scratch: s, v, mv of E doubles; keep, gs of G; chosen of E; sel of K
+ *   out_w[K], out_i[K]: weights and expert ids
+ *   margin[2]: {K-th minus (K+1)-th masked choice score,
+ *               KG-th minus (KG+1)-th group score}; +inf when undefined. */
+static void select_token(const double *L, const float *bias, int64_t E, int G,
+                         int KG, int K, double route_scale, int order,
+                         const gate_opts *opt, double *s, double *v,
+                         double *mv, int *keep, double *gs, int *chosen,
+                         int64_t *sel, double *out_w, int32_t *out_i,
+                         double *margin)
+{
+    const int64_t S = E / G;
+
+    /* Steps 2-4: affinities, choice scores, group scores. */
+    token_scores(L, bias, E, G, opt, s, v, gs);
+
+    /* Step 5: group keep mask. */
+    for (int g = 0; g < G; ++g) keep[g] = 1;
+    margin[1] = INFINITY;
+    if (G > 1) {
         /* a group is kept when fewer than KG groups precede it */
         for (int g = 0; g < G; ++g) {
             int ahead = 0;
@@ -306,6 +323,34 @@ int oracle_select(const double *logits, const float *bias, int64_t T,
                              margins ? margins + 2 * t : mdummy);
         }
         free(s); free(v); free(mv); free(gs); free(keep); free(chosen); free(sel);
+    }
+    return failed ? ORACLE_EINVAL : ORACLE_OK;
+}
+
+/* Steps 2-4 from precomputed float64 logits [T, E]: affinities s [T, E],
+ * choice scores v [T, E] and group scores gs [T, G] (gs is not written when
+ * G == 1).  bias may be NULL; score_func as in oracle_select. */
+int oracle_scores(const double *logits, const float *bias, int64_t T, int64_t E,
+                  int G, int score_func, double *s, double *v, double *gs)
+{
+    if (E <= 0 || G <= 0 || E % G != 0) return ORACLE_EINVAL;
+    if (G > 1 && E / G < 2) return ORACLE_EINVAL;
+    if (score_func != 0 && score_func != 1) return ORACLE_EINVAL;
+    const gate_opts opt = {score_func, 0, 0, 0.0};
+    int failed = 0;
+#pragma omp parallel
+    {
+        double *gdummy = malloc(sizeof(double) * G);
+        if (!gdummy) {
+#pragma omp atomic write
+            failed = 1;
+        } else {
+#pragma omp for schedule(static)
+            for (int64_t t = 0; t < T; ++t)
+                token_scores(logits + t * E, bias, E, G, &opt, s + t * E, v + t * E,
+                             G > 1 ? gs + t * G : gdummy);
+        }
+        free(gdummy);
     }
     return failed ? ORACLE_EINVAL : ORACLE_OK;
 }

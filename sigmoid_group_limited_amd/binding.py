@@ -2,8 +2,10 @@
 
 Argument marshalling only: every step of the gate and the dispatch runs in the
 HIP kernels of the library.  PyTorch supplies device memory (tensors) and the
-current stream.  The library is loaded on first use; when it is missing or
-cannot be loaded the call raises -- there is no fallback path.
+current stream.  Workspaces and outputs the wrappers allocate themselves are
+allocated on the stream the call runs on (``stream=``, else the current
+one).  The library is loaded on first use; when it is missing or cannot be
+loaded the call raises -- there is no fallback path.
 """
 from __future__ import annotations
 
@@ -140,6 +142,22 @@ def _stream(stream) -> int | None:
     return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
 
 
+def _on_stream(stream):
+    """Context in which the wrappers allocate their workspace and outputs:
+    the stream the kernels will run on.  The caching allocator ties a block
+    to the stream current at its allocation, so a workspace released on
+    return is not handed to other work before this call's kernels are done
+    with it.  stream may be None (the current stream), a torch stream, or a
+    raw hipStream_t handle."""
+    import contextlib
+    import torch
+    if stream is None:
+        return contextlib.nullcontext()
+    if not isinstance(stream, torch.cuda.Stream):
+        stream = torch.cuda.ExternalStream(int(stream))
+    return torch.cuda.stream(stream)
+
+
 def _check_dev(name, t, dtype_bytes=None, numel=None):
     if t is None:
         return
@@ -167,12 +185,13 @@ def siggate_forward(x, W, bias, cfg: Cfg, weights=None, indices=None, ws=None, s
     import torch
     T, K = cfg.T, cfg.top_k
     dev = x.device
-    if weights is None:
-        weights = torch.empty((T, K), dtype=torch.float32, device=dev)
-    if indices is None:
-        indices = torch.empty((T, K), dtype=torch.int32, device=dev)
-    if ws is None:
-        ws = workspace(cfg, dev)
+    with _on_stream(stream):
+        if weights is None:
+            weights = torch.empty((T, K), dtype=torch.float32, device=dev)
+        if indices is None:
+            indices = torch.empty((T, K), dtype=torch.int32, device=dev)
+        if ws is None:
+            ws = workspace(cfg, dev)
     _check_dev("x", x, 2, cfg.T * cfg.d)
     _check_dev("W", W, 4, cfg.E * cfg.d)
     if bias is not None:
@@ -191,10 +210,11 @@ def siggate_forward(x, W, bias, cfg: Cfg, weights=None, indices=None, ws=None, s
 def siggate_logits(x, W, cfg: Cfg, logits=None, ws=None, stream=None):
     """float32 logits [T, E] as siggate_forward computes them."""
     import torch
-    if logits is None:
-        logits = torch.empty((cfg.T, cfg.E), dtype=torch.float32, device=x.device)
-    if ws is None:
-        ws = workspace(cfg, x.device)
+    with _on_stream(stream):
+        if logits is None:
+            logits = torch.empty((cfg.T, cfg.E), dtype=torch.float32, device=x.device)
+        if ws is None:
+            ws = workspace(cfg, x.device)
     _check_dev("x", x, 2, cfg.T * cfg.d)
     _check_dev("W", W, 4, cfg.E * cfg.d)
     _check_dev("logits", logits, 4, cfg.T * cfg.E)
@@ -224,15 +244,16 @@ def siggate_dispatch(x, indices, cfg: Cfg, out: DispatchOut | None = None, ws=No
     import torch
     T, K, E, d = cfg.T, cfg.top_k, cfg.E, cfg.d
     dev = x.device
-    if out is None:
-        out = DispatchOut(
-            torch.empty(E, dtype=torch.int32, device=dev),
-            torch.empty(E + 1, dtype=torch.int32, device=dev) if with_offsets else None,
-            torch.empty(T * K, dtype=torch.int32, device=dev),
-            torch.empty(T * K, dtype=torch.int32, device=dev) if with_dest else None,
-            torch.empty((T * K, d), dtype=x.dtype, device=dev))
-    if ws is None:
-        ws = workspace(cfg, dev)
+    with _on_stream(stream):
+        if out is None:
+            out = DispatchOut(
+                torch.empty(E, dtype=torch.int32, device=dev),
+                torch.empty(E + 1, dtype=torch.int32, device=dev) if with_offsets else None,
+                torch.empty(T * K, dtype=torch.int32, device=dev),
+                torch.empty(T * K, dtype=torch.int32, device=dev) if with_dest else None,
+                torch.empty((T * K, d), dtype=x.dtype, device=dev))
+        if ws is None:
+            ws = workspace(cfg, dev)
     _check_dev("x", x, 2, T * d)
     _check_dev("indices", indices, 4, T * K)
     _check_dev("tokens_per_expert", out.tokens_per_expert, 4, E)
@@ -256,7 +277,8 @@ def siggate_combine(expert_out, weights, dest, cfg: Cfg, y=None, stream=None):
     import torch
     T, K, d = cfg.T, cfg.top_k, cfg.d
     if y is None:
-        y = torch.empty((T, d), dtype=expert_out.dtype, device=expert_out.device)
+        with _on_stream(stream):
+            y = torch.empty((T, d), dtype=expert_out.dtype, device=expert_out.device)
     _check_dev("expert_out", expert_out, 2, T * K * d)
     _check_dev("weights", weights, 4, T * K)
     _check_dev("dest", dest, 4, T * K)
@@ -277,8 +299,9 @@ def siggate_ep_send_splits(tokens_per_expert, ep_size: int, stream=None):
     E = tokens_per_expert.numel()
     _check_dev("tokens_per_expert", tokens_per_expert, 4, E)
     dev = tokens_per_expert.device
-    counts = torch.empty(ep_size, dtype=torch.int32, device=dev)
-    offsets = torch.empty(ep_size + 1, dtype=torch.int32, device=dev)
+    with _on_stream(stream):
+        counts = torch.empty(ep_size, dtype=torch.int32, device=dev)
+        offsets = torch.empty(ep_size + 1, dtype=torch.int32, device=dev)
     rc = load_library().siggate_ep_send_splits(_ptr(tokens_per_expert), E, ep_size,
                                                _ptr(counts), _ptr(offsets), _stream(stream))
     if rc != SIGGATE_OK:
@@ -292,8 +315,9 @@ def siggate_ep_regroup(counts, capacity: int, stream=None):
     R, per = counts.shape
     _check_dev("counts", counts, 4, R * per)
     dev = counts.device
-    local = torch.empty(per, dtype=torch.int32, device=dev)
-    regroup = torch.empty(max(capacity, 1), dtype=torch.int32, device=dev)
+    with _on_stream(stream):
+        local = torch.empty(per, dtype=torch.int32, device=dev)
+        regroup = torch.empty(max(capacity, 1), dtype=torch.int32, device=dev)
     rc = load_library().siggate_ep_regroup(_ptr(counts), R, per, capacity, _ptr(local),
                                            _ptr(regroup), _stream(stream))
     if rc != SIGGATE_OK:
@@ -313,13 +337,14 @@ def siggate_ep_dedup(indices, cfg: Cfg, ep_size: int, ws=None, stream=None):
     T, K = cfg.T, cfg.top_k
     _check_dev("indices", indices, 4, T * K)
     dev = indices.device
-    if ws is None:
-        ws = torch.empty(max(256, siggate_ep_workspace_bytes(cfg, ep_size)), dtype=torch.uint8,
-                         device=dev)
-    rcnt = torch.empty(ep_size, dtype=torch.int32, device=dev)
-    roff = torch.empty(ep_size + 1, dtype=torch.int32, device=dev)
-    send = torch.empty(max(T * K, 1), dtype=torch.int32, device=dev)
-    slot = torch.empty(max(T * K, 1), dtype=torch.int32, device=dev)
+    with _on_stream(stream):
+        if ws is None:
+            ws = torch.empty(max(256, siggate_ep_workspace_bytes(cfg, ep_size)),
+                             dtype=torch.uint8, device=dev)
+        rcnt = torch.empty(ep_size, dtype=torch.int32, device=dev)
+        roff = torch.empty(ep_size + 1, dtype=torch.int32, device=dev)
+        send = torch.empty(max(T * K, 1), dtype=torch.int32, device=dev)
+        slot = torch.empty(max(T * K, 1), dtype=torch.int32, device=dev)
     c = cfg.c()
     rc = load_library().siggate_ep_dedup(_ptr(indices), ctypes.byref(c), ep_size, _ptr(rcnt),
                                          _ptr(roff), _ptr(send), _ptr(slot), _ptr(ws),

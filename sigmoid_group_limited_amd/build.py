@@ -14,14 +14,18 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIBRARY = os.path.join(PKG, "libsiggate.so")
+# exports only the siggate_* functions
+VERSION_SCRIPT = os.path.join(CSRC, "siggate.map")
 EXAMPLE_SOURCE = os.path.join(PKG, "examples", "route_c.cpp")
 EXAMPLE = os.path.join(PKG, "route_c")
 SOURCES = ["gate.hip", "logits_x3.hip", "dispatch.hip", "combine.hip", "ep.hip", "api.hip"]
 ARCH = "gfx950"
 
-# Packed fp32 arithmetic is switched off for all device code.
+# Packed fp32 arithmetic is switched off for all device code.  Symbols are
+# hidden by default: the library exports only the C ABI of siggate.h.
 HIPCC_FLAGS = ["-O3", "-std=c++17", "-fPIC", "-shared", f"--offload-arch={ARCH}",
-               "-Wall", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+               "-Wall", "-fvisibility=hidden", "-Xclang", "-target-feature", "-Xclang",
+               "-packed-fp32-ops"]
 
 
 def hipcc() -> str:
@@ -35,7 +39,8 @@ def build(verbose: bool = False) -> str:
     """Compile every HIP source into ``libsiggate.so`` next to this file."""
     srcs = [os.path.join(CSRC, s) for s in SOURCES]
     tmp = LIBRARY + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC, *srcs, "-o", tmp]
+    cmd = [hipcc(), *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC, *srcs,
+           f"-Wl,--version-script={VERSION_SCRIPT}", "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)

@@ -2,7 +2,11 @@
 // argument checks, workspace layout and kernel launches.  Host code only.
 #include <string.h>
 
+// The library is built with hidden visibility: the functions siggate.h
+// declares are its only exported symbols.
+#pragma GCC visibility push(default)
 #include "siggate.h"
+#pragma GCC visibility pop
 #include "siggate_internal.h"
 
 using namespace siggate;

@@ -13,8 +13,11 @@
 // significant bits), mid the same of the remainder W - hi, and lo = W - hi -
 // mid, which has at most 8 significant bits left and is itself a bfloat16.
 // Each of the three differences is exact (the operands share sign and
-// exponent range), so the split loses nothing for |W| >= 2^-110 (lo stays a
-// normal number).  The products x*hi, x*mid and x*lo are exact in float32
+// exponent range), so the split loses nothing.  A nonzero part can be as
+// small as the last significant bit of W, 2^-23 |W| rounded down to a power
+// of two, so every part is a normal number for |W| >= 2^-103; below that a
+// part may be subnormal, and exactness then rests on the matrix cores
+// keeping subnormal bfloat16 inputs.  The products x*hi, x*mid and x*lo are exact in float32
 // (8 x 8 significant bits), and v_mfma_f32_16x16x32_bf16 adds them into
 // float32 accumulators, so L carries float32 accumulation error only, as on
 // the float32 matrix cores, at 16x their per-instruction rate (3 products

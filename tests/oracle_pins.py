@@ -492,10 +492,49 @@ def pin_ep_dedup(o):
         assert np.array_equal(rank_of_slot, idx.ravel() // per)
 
 
+def pin_scores(o):
+    """The scores the oracle ranks (its ``scores`` entry point, the code its
+    selection runs): affinities are scipy's expit (or softmax) of the
+    logits, choice scores add the bias (nothing without one), and a group
+    scores the sum of its two largest choice scores (numpy sort), or its
+    largest without a bias."""
+    from scipy.special import softmax
+    rng = np.random.default_rng(32)
+    for (E, G) in [(256, 8), (384, 1), (16, 4), (128, 64)]:
+        T = 9
+        L = rng.standard_normal((T, E)) * 2.0
+        b = rng.uniform(-0.3, 0.3, size=E).astype(np.float32)
+        S = E // G
+        sc = o.scores(L, b, G)
+        assert np.allclose(sc.affinity, expit(L), rtol=1e-14, atol=0)
+        assert np.allclose(sc.choice, expit(L) + b.astype(np.float64), rtol=1e-14, atol=1e-16)
+        if G > 1:
+            top2 = np.sort(sc.choice.reshape(T, G, S), axis=2)[:, :, -2:].sum(axis=2)
+            assert np.array_equal(sc.group, top2)
+        else:
+            assert sc.group.shape == (T, 0)
+        sm = o.scores(L, None, G, score_func=1)
+        assert np.allclose(sm.affinity, softmax(L, axis=1), rtol=1e-12, atol=0)
+        assert np.array_equal(sm.choice, sm.affinity)
+        if G > 1:
+            assert np.array_equal(sm.group, sm.choice.reshape(T, G, S).max(axis=2))
+    # the selection ranks exactly these scores: its winners are the top set
+    # of the choice scores inside the best groups
+    E, G, KG, K = 64, 8, 3, 6
+    L = rng.standard_normal((50, E))
+    b = rng.uniform(-0.05, 0.05, size=E).astype(np.float32)
+    r = o.select(L, b, G, KG, K, 2.5, with_scores=True)
+    for t in range(50):
+        gs = r.scores.group[t]
+        kept = sorted(range(G), key=lambda g: (-gs[g], g))[:KG]
+        pool = [e for e in range(E) if e // (E // G) in kept]
+        assert _is_top_set(set(r.indices[t].tolist()), r.scores.choice[t], pool)
+
+
 ALL_PINS = [pin_exact_integer_logits, pin_logits_vs_matmul, pin_brute_force_selection,
             pin_zero_input_closed_form, pin_bias_shift_invariance,
             pin_weights_follow_unbiased_sigmoid, pin_winners_in_kept_groups,
             pin_single_group_no_bias_is_topk_of_logits, pin_permutation_equivariance,
             pin_margins, pin_selection_order, pin_dispatch, pin_softmax_scores,
             pin_no_bias_group_max, pin_renorm_off, pin_mask_zero, pin_denominator_epsilon,
-            pin_combine, pin_ep_send_splits, pin_ep_regroup, pin_ep_dedup]
+            pin_combine, pin_ep_send_splits, pin_ep_regroup, pin_ep_dedup, pin_scores]

@@ -35,11 +35,16 @@ def dev_inputs(gi, device="cuda"):
 
 
 def compare_gate(w_gpu: np.ndarray, i_gpu: np.ndarray, ref, route_scale: float,
-                 rows: np.ndarray | None = None, check_sum: bool = True):
+                 rows: np.ndarray | None = None, check_sum: bool = True, *,
+                 topk_group: int | None = None, renorm: bool = True,
+                 mask_zero: int = 0, denom_eps: float = 0.0):
     """Compare GPU weights/indices (full [T, K] arrays, or ``rows`` of them)
     with an oracle result on the same rows.  Returns a stats dict; raises
-    AssertionError on a non-exempt index mismatch or a weight outside
-    tolerance."""
+    AssertionError on a non-exempt index mismatch, a weight outside
+    tolerance, or an exempt token whose GPU selection is not a valid
+    resolution of its near-tie (see ``check_near_tie``; that check needs the
+    oracle's scores, ``ref.scores``, and ``topk_group`` when there are
+    several groups)."""
     if rows is not None:
         w_gpu, i_gpu = w_gpu[rows], i_gpu[rows]
     margin = np.minimum(ref.margins[:, 0], ref.margins[:, 1])
@@ -57,12 +62,84 @@ def compare_gate(w_gpu: np.ndarray, i_gpu: np.ndarray, ref, route_scale: float,
     rel = np.abs(wg - wr) / np.maximum(np.abs(wr), 1e-30)
     stats["weight_max_rel"] = float(rel.max()) if rel.size else 0.0
     assert stats["weight_max_rel"] <= WEIGHT_RTOL, stats
+    # exempt tokens that differ: the GPU's choice must be one of the valid
+    # resolutions of the near-tie
+    differ = np.nonzero(exempt & ~same)[0]
+    stats["exempt_differ_valid"] = 0
+    for r in differ:
+        assert ref.scores is not None, \
+            "an exempt token differs from the oracle; its check needs the oracle's scores"
+        G = max(1, ref.scores.group.shape[1])
+        assert G == 1 or topk_group is not None, "the near-tie check needs topk_group"
+        check_near_tie(i_gpu[r], w_gpu[r], ref.scores.affinity[r], ref.scores.choice[r],
+                       ref.scores.group[r] if G > 1 else None, topk_group or 1,
+                       route_scale, renorm, mask_zero, denom_eps)
+        stats["exempt_differ_valid"] += 1
     # properties that hold for every token, exempt or not
     assert np.all(w_gpu >= 0)
     if check_sum:
         sums = w_gpu.astype(np.float64).sum(1)
         assert np.allclose(sums, route_scale, rtol=1e-5, atol=0), "weights do not sum to route_scale"
     return stats
+
+
+def _kept_candidates(ids: np.ndarray, gs: np.ndarray, KG: int, S: int):
+    """Kept-group sets that a near-tie resolution might have used: the
+    groups of the winners filled up with the best other groups, and the
+    best KG groups themselves (ties to the lower group index)."""
+    G = len(gs)
+    rank = sorted(range(G), key=lambda g: (-gs[g], g))
+    out = [set(rank[:KG])]
+    gw = {int(e) // S for e in ids}
+    if len(gw) <= KG:
+        fill = [g for g in rank if g not in gw][:KG - len(gw)]
+        out.insert(0, gw | set(fill))
+    return out
+
+
+def check_near_tie(ids: np.ndarray, w: np.ndarray, s: np.ndarray, v: np.ndarray,
+                   gs: np.ndarray | None, topk_group: int, route_scale: float,
+                   renorm: bool = True, mask_zero: int = 0, denom_eps: float = 0.0,
+                   tol: float = EXEMPT_MARGIN):
+    """One token whose oracle margin is below the exemption threshold and
+    whose GPU selection differs from the oracle's.  The selection is valid
+    when, against the oracle's float64 scores, some set of topk_group kept
+    groups has every kept group scoring at least every dropped group's score
+    minus ``tol``, and under it every winner's masked choice score is at
+    least every loser's minus ``tol``.  The weights must then equal the
+    oracle's weights recomputed on the GPU's set, to the weight tolerance."""
+    ids = np.asarray(ids, dtype=np.int64)
+    K, E = len(ids), len(v)
+    assert len(np.unique(ids)) == K and ids.min() >= 0 and ids.max() < E
+    lose = np.ones(E, bool)
+    lose[ids] = False
+    fill = 0.0 if mask_zero else -np.inf
+    ok = False
+    if gs is None:
+        cands = [None]
+    else:
+        S = E // len(gs)
+        cands = _kept_candidates(ids, gs, topk_group, S)
+    for kept in cands:
+        if kept is None:
+            vm = v
+        else:
+            drop = [g for g in range(len(gs)) if g not in kept]
+            if drop and min(gs[g] for g in kept) < max(gs[g] for g in drop) - tol:
+                continue
+            inside = np.isin(np.arange(E) // S, list(kept))
+            vm = np.where(inside, v, fill)
+        if not np.all(np.isfinite(vm[ids])):
+            continue
+        if not lose.any() or vm[ids].min() >= vm[lose].max() - tol:
+            ok = True
+            break
+    assert ok, (f"exempt token: GPU experts {ids.tolist()} are not a valid resolution of "
+                f"the near-tie (choice scores {v[ids].tolist()})")
+    ss = s[ids]
+    want = route_scale * ss / (ss.sum() + denom_eps) if renorm else route_scale * ss
+    rel = np.abs(np.asarray(w, np.float64) - want) / np.maximum(np.abs(want), 1e-30)
+    assert rel.max() <= WEIGHT_RTOL, f"exempt token: weights off by {rel.max():.2e} relative"
 
 
 def check_rows_valid(i_gpu: np.ndarray, E: int, n_group: int, topk_group: int,
@@ -96,13 +173,36 @@ def compare_dispatch(out, ref, indices: np.ndarray, x: np.ndarray, K: int,
         inv[ref.perm] = np.arange(len(ref.perm), dtype=ref.perm.dtype)
         assert np.array_equal(dest, inv), "dest is not the inverse of perm"
     n = len(ref.perm)
-    rows = np.arange(n) if sample_rows is None else sample_rows
+    if sample_rows is None:
+        compare_rows_full(out.permuted_x, x, ref.perm, K, oracle)
+        return
+    rows = sample_rows
     if len(rows):
         import torch
         got = out.permuted_x[torch.from_numpy(rows).to(out.permuted_x.device)]
         got = got.view(torch.int16).cpu().numpy().view(np.uint16)
         want = oracle.gather_rows(x, ref.perm, K, rows)
         assert np.array_equal(got, want), "permuted_x rows differ"
+
+
+def compare_rows_full(permuted_x, x: np.ndarray, perm: np.ndarray, K: int, oracle,
+                      chunk_bytes: int = 1 << 28):
+    """Every row of the GPU's permuted_x against the oracle's row gather on
+    the same permutation, copied to the host in chunks of about
+    ``chunk_bytes``."""
+    import torch
+    n = len(perm)
+    d = x.shape[1]
+    step = max(1, chunk_bytes // (2 * d))
+    flat = permuted_x.view(torch.int16)
+    for p0 in range(0, n, step):
+        p1 = min(n, p0 + step)
+        got = flat[p0:p1].cpu().numpy().view(np.uint16)
+        want = oracle.gather_rows(x, perm, K, np.arange(p0, p1))
+        if not np.array_equal(got, want):
+            bad = np.nonzero(np.any(got != want, axis=1))[0]
+            raise AssertionError(f"permuted_x rows differ: {len(bad)} rows in [{p0}, {p1}), "
+                                 f"first {p0 + int(bad[0])}")
 
 
 def combine_tolerance(o, outs, w64, dest, y64, K):

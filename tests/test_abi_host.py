@@ -41,6 +41,16 @@ def test_exports_every_declared_symbol(lib):
         assert ctypes.cast(getattr(lib, n), ctypes.c_void_p).value
 
 
+def test_exports_nothing_else(lib):
+    """The library's dynamic symbol table defines exactly the functions
+    siggate.h declares: internal C++ symbols stay hidden."""
+    import subprocess
+    res = subprocess.run(["nm", "-D", "--defined-only", binding.LIBRARY],
+                         capture_output=True, text=True, check=True)
+    defined = sorted(ln.split()[-1] for ln in res.stdout.splitlines() if ln.strip())
+    assert defined == declared_functions()
+
+
 def test_status_strings(lib):
     for code in (0, -1, -2, -3, -4):
         assert sg.siggate_status_str(code).startswith("SIGGATE_")

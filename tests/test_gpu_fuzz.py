@@ -73,18 +73,21 @@ def test_random_configuration(o, seed, lp):
     w_np, i_np = w.cpu().numpy(), i.cpu().numpy()
     ref = o.gate(gi.x, gi.W, None if no_bias else gi.bias, gc.n_group, gc.topk_group, gc.top_k,
                  gc.route_scale, cfg.order, score_func=cfg.score_func, renorm=cfg.renorm,
-                 mask_zero=cfg.mask_zero, denom_eps=cfg.denom_eps)
+                 mask_zero=cfg.mask_zero, denom_eps=cfg.denom_eps, with_scores=True)
     renorm = cfg.renorm == 1 or (cfg.renorm == 0 and cfg.score_func == 0)
+    tie = dict(topk_group=gc.topk_group, renorm=renorm, mask_zero=cfg.mask_zero,
+               denom_eps=cfg.denom_eps)
     if cfg.order == 0:
-        stats = compare_gate(w_np, i_np, ref, gc.route_scale, check_sum=renorm)
+        stats = compare_gate(w_np, i_np, ref, gc.route_scale, check_sum=renorm, **tie)
     else:
         # compare as sets (sorted by id); the order itself is pinned elsewhere
         si = np.argsort(i_np, axis=1, kind="stable")
         sr = np.argsort(ref.indices, axis=1, kind="stable")
         ref_sorted = oracle.GateResult(np.take_along_axis(ref.weights, sr, 1),
-                                       np.take_along_axis(ref.indices, sr, 1), ref.margins)
+                                       np.take_along_axis(ref.indices, sr, 1), ref.margins,
+                                       ref.scores)
         stats = compare_gate(np.take_along_axis(w_np, si, 1), np.take_along_axis(i_np, si, 1),
-                             ref_sorted, gc.route_scale, check_sum=renorm)
+                             ref_sorted, gc.route_scale, check_sum=renorm, **tie)
     assert i_np.min() >= 0 and i_np.max() < gc.n_experts
     say(f"    {stats}")
     out = sg.siggate_dispatch(x, i, cfg)

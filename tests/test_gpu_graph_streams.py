@@ -115,3 +115,38 @@ def test_concurrent_streams_match_sequential(lp):
     for want, bufs in zip(seq, par_bufs):
         for k, (a, c) in enumerate(zip(_snapshot(bufs), want)):
             assert torch.equal(a, c), f"output {k} differs from the sequential run"
+
+
+@pytest.mark.parametrize("lp", [0, 1], ids=["fp32", "bf16x3"])
+@pytest.mark.parametrize("raw", [False, True], ids=["torch_stream", "raw_handle"])
+def test_explicit_stream_without_workspace(lp, raw):
+    """A call given stream= but no workspace allocates it (and its outputs)
+    on that stream: work queued right after on the current stream, which
+    allocates and overwrites memory of the same sizes, cannot take the
+    workspace while the call's kernels still use it."""
+    gc = wl.KIMI_K2
+    T, d = 4096, 7168                     # split GEMM: partial logits in the workspace
+    cfg = sg.Cfg(T, d, gc.n_experts, gc.n_group, gc.topk_group, gc.top_k, gc.route_scale,
+                 logits_path=lp)
+    gi = wl.make_gate_inputs(T, d, gc, seed=41)
+    x = torch.from_numpy(gi.x.view(np.int16)).cuda().view(torch.bfloat16)
+    W = torch.from_numpy(gi.W).cuda()
+    b = torch.from_numpy(gi.bias).cuda()
+    w0, i0 = sg.siggate_forward(x, W, b, cfg)
+    out0 = sg.siggate_dispatch(x, i0, cfg)
+    torch.cuda.synchronize()
+    nbytes = max(256, sg.siggate_workspace_bytes(cfg))
+    side = torch.cuda.Stream()
+    handle = int(side.cuda_stream) if raw else side
+    for rep in range(3):
+        side.wait_stream(torch.cuda.current_stream())
+        w, i = sg.siggate_forward(x, W, b, cfg, stream=handle)
+        junk = [torch.full((nbytes // 4,), -1.0, device="cuda") for _ in range(4)]
+        side.synchronize()
+        out = sg.siggate_dispatch(x, i, cfg, stream=handle)
+        junk += [torch.full((nbytes // 4,), 7.0, device="cuda") for _ in range(4)]
+        torch.cuda.synchronize()
+        del junk
+        assert torch.equal(w, w0) and torch.equal(i, i0), f"rep {rep}: gate differs"
+        assert torch.equal(out.perm, out0.perm), f"rep {rep}: perm differs"
+        assert torch.equal(out.permuted_x, out0.permuted_x), f"rep {rep}: rows differ"

@@ -69,7 +69,8 @@ def test_offsets_past_32_bits(o):
     rng = np.random.default_rng(13)
     rows = np.unique(np.r_[0, first_far - 1, first_far, T - 1,
                            rng.integers(first_far, T, 384), rng.integers(0, T, 128)])
-    ref = o.gate(gi.x[rows % R], gi.W, gi.bias, gc.n_group, gc.topk_group, K, gc.route_scale)
+    ref = o.gate(gi.x[rows % R], gi.W, gi.bias, gc.n_group, gc.topk_group, K, gc.route_scale,
+                 with_scores=True)
 
     base = sg.Cfg(T, d, E, gc.n_group, gc.topk_group, K, gc.route_scale)
     wg = ig = None
@@ -84,7 +85,7 @@ def test_offsets_past_32_bits(o):
         same_row = np.arange(T) % R
         assert np.array_equal(i_np, i_np[same_row]) and np.array_equal(w_np, w_np[same_row]), \
             "repeated rows of x were routed differently"
-        stats = compare_gate(w_np, i_np, ref, gc.route_scale, rows)
+        stats = compare_gate(w_np, i_np, ref, gc.route_scale, rows, topk_group=gc.topk_group)
         say(f"    gate logits_path={lp}: {stats}")
         if lp == 0:
             wg, ig, idx = w, i, i_np

@@ -64,9 +64,10 @@ def test_gate_variant(o, name, gc, T, d, opts, bias_kind, lp):
     w, i = w.cpu().numpy(), i.cpu().numpy()
     ref = o.gate(gi.x, gi.W, bias, gc.n_group, gc.topk_group, gc.top_k, gc.route_scale,
                  score_func=cfg.score_func, renorm=cfg.renorm, mask_zero=cfg.mask_zero,
-                 denom_eps=cfg.denom_eps)
+                 denom_eps=cfg.denom_eps, with_scores=True)
     renorm = cfg.renorm == 1 or (cfg.renorm == 0 and cfg.score_func == 0)
-    stats = compare_gate(w, i, ref, gc.route_scale, check_sum=renorm)
+    stats = compare_gate(w, i, ref, gc.route_scale, check_sum=renorm, topk_group=gc.topk_group,
+                         renorm=renorm, mask_zero=cfg.mask_zero, denom_eps=cfg.denom_eps)
     assert i.min() >= 0 and i.max() < gc.n_experts
     if not cfg.mask_zero:
         check_rows_valid(i, gc.n_experts, gc.n_group, gc.topk_group)
