@@ -99,8 +99,13 @@ typedef enum siggate_status {
     SIGGATE_EINVAL = -1,        /* invalid configuration or null/misaligned pointer */
     SIGGATE_EUNSUPPORTED = -2,  /* valid configuration this library does not build  */
     SIGGATE_EWORKSPACE = -3,    /* workspace smaller than siggate_workspace_bytes   */
-    SIGGATE_EHIP = -4           /* the HIP runtime reported a launch error          */
+    SIGGATE_EHIP = -4,          /* the HIP runtime reported a launch error          */
+    SIGGATE_ESCRATCH = -5       /* siggate_forward_noalloc: the configuration needs
+                                   more than SIGGATE_SCRATCH_BYTES of workspace     */
 } siggate_status_t;
+
+/* Size of the static device scratch of siggate_forward_noalloc: 64 MiB. */
+#define SIGGATE_SCRATCH_BYTES ((size_t)64 << 20)
 
 /* Bytes of device workspace that siggate_forward and siggate_dispatch need
  * for this configuration: the larger of the two needs, counting only a call
@@ -128,6 +133,28 @@ siggate_status_t siggate_forward(const void *x, const float *W, const float *bia
                                  const siggate_cfg_t *cfg, float *weights,
                                  int32_t *indices, void *ws, size_t ws_bytes,
                                  void *stream);
+
+/* Gate that allocates nothing, for callers that cannot allocate device
+ * memory or pass a workspace: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  Same computation, kernels and
+ * results as siggate_forward; the workspace is the library's static device
+ * array of SIGGATE_SCRATCH_BYTES, one copy per device, allocated when the
+ * library's code is loaded on that device and held until the process ends.
+ *   - The stream must belong to the current device.
+ *   - Every call on one device shares that device's scratch, so calls that
+ *     overlap in time on one device (several streams, several host threads)
+ *     race and give undefined results; calls on one stream are ordered.
+ *   - Configurations whose gate workspace exceeds SIGGATE_SCRATCH_BYTES
+ *     return SIGGATE_ESCRATCH before anything is enqueued.  At d = 7168
+ *     every T fits on logits_path 0; on logits_path 1 every T <= 10880
+ *     (E = 384) or <= 16384 (E = 256) fits, and larger batches fit or not
+ *     by the plan's slice count (siggate_workspace_bytes tells).
+ *   - The first call on a device looks up the scratch's device address
+ *     (hipGetSymbolAddress); it calls no hipMalloc or hipFree, then or ever.
+ * Other arguments and errors as siggate_forward. */
+siggate_status_t siggate_forward_noalloc(const void *x, const float *W, const float *bias,
+                                         const siggate_cfg_t *cfg, float *weights,
+                                         int32_t *indices, void *stream);
 
 /* Dispatch.
  *   x                  bfloat16 [T, d]

@@ -9,9 +9,11 @@ the first call does, and raises if it is not built.
 from .binding import (Cfg, DispatchOut, SiggateError, load_library, siggate_combine,
                       siggate_dispatch, siggate_ep_dedup, siggate_ep_regroup,
                       siggate_ep_send_splits, siggate_ep_workspace_bytes, siggate_forward,
-                      siggate_logits, siggate_status_str, siggate_workspace_bytes, workspace)
+                      siggate_forward_noalloc, siggate_logits, siggate_status_str,
+                      siggate_workspace_bytes, workspace)
 
 __all__ = ["Cfg", "DispatchOut", "SiggateError", "load_library", "siggate_combine",
            "siggate_dispatch", "siggate_ep_dedup", "siggate_ep_regroup",
            "siggate_ep_send_splits", "siggate_ep_workspace_bytes", "siggate_forward",
-           "siggate_logits", "siggate_status_str", "siggate_workspace_bytes", "workspace"]
+           "siggate_forward_noalloc", "siggate_logits", "siggate_status_str",
+           "siggate_workspace_bytes", "workspace"]

@@ -22,9 +22,12 @@ SIGGATE_EINVAL = -1
 SIGGATE_EUNSUPPORTED = -2
 SIGGATE_EWORKSPACE = -3
 SIGGATE_EHIP = -4
+SIGGATE_ESCRATCH = -5
+SIGGATE_SCRATCH_BYTES = 64 << 20
 
 # Symbols declared in include/siggate.h
-EXPORTS = ("siggate_workspace_bytes", "siggate_forward", "siggate_dispatch",
+EXPORTS = ("siggate_workspace_bytes", "siggate_forward", "siggate_forward_noalloc",
+           "siggate_dispatch",
            "siggate_combine", "siggate_ep_send_splits", "siggate_ep_regroup",
            "siggate_ep_workspace_bytes", "siggate_ep_dedup", "siggate_logits",
            "siggate_status_str")
@@ -97,6 +100,8 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
     lib.siggate_workspace_bytes.argtypes = [cfgp]
     lib.siggate_forward.restype = ctypes.c_int
     lib.siggate_forward.argtypes = [vp, vp, vp, cfgp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.siggate_forward_noalloc.restype = ctypes.c_int
+    lib.siggate_forward_noalloc.argtypes = [vp, vp, vp, cfgp, vp, vp, vp]
     lib.siggate_dispatch.restype = ctypes.c_int
     lib.siggate_dispatch.argtypes = [vp, vp, cfgp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.siggate_combine.restype = ctypes.c_int
@@ -204,6 +209,32 @@ def siggate_forward(x, W, bias, cfg: Cfg, weights=None, indices=None, ws=None, s
                                         ws.numel() * ws.element_size(), _stream(stream))
     if rc != SIGGATE_OK:
         raise SiggateError(rc, "siggate_forward")
+    return weights, indices
+
+
+def siggate_forward_noalloc(x, W, bias, cfg: Cfg, weights=None, indices=None, stream=None):
+    """Gate on the library's static device scratch (no workspace argument;
+    the library allocates nothing).  Outputs not given are allocated here,
+    on the call's stream."""
+    import torch
+    T, K = cfg.T, cfg.top_k
+    dev = x.device
+    with _on_stream(stream):
+        if weights is None:
+            weights = torch.empty((T, K), dtype=torch.float32, device=dev)
+        if indices is None:
+            indices = torch.empty((T, K), dtype=torch.int32, device=dev)
+    _check_dev("x", x, 2, cfg.T * cfg.d)
+    _check_dev("W", W, 4, cfg.E * cfg.d)
+    if bias is not None:
+        _check_dev("bias", bias, 4, cfg.E)
+    _check_dev("weights", weights, 4, T * K)
+    _check_dev("indices", indices, 4, T * K)
+    c = cfg.c()
+    rc = load_library().siggate_forward_noalloc(_ptr(x), _ptr(W), _ptr(bias), ctypes.byref(c),
+                                                _ptr(weights), _ptr(indices), _stream(stream))
+    if rc != SIGGATE_OK:
+        raise SiggateError(rc, "siggate_forward_noalloc")
     return weights, indices
 
 

@@ -2,6 +2,9 @@
 // argument checks, workspace layout and kernel launches.  Host code only.
 #include <string.h>
 
+#include <atomic>
+#include <mutex>
+
 // The library is built with hidden visibility: the functions siggate.h
 // declares are its only exported symbols.
 #pragma GCC visibility push(default)
@@ -55,6 +58,40 @@ siggate_status_t check_dispatch_cfg(const siggate_cfg_t *c)
 size_t forward_bytes(const siggate_cfg_t *c)
 {
     return align256(plan_gate(c->T, c->d, c->E, c->logits_path).partial_bytes);
+}
+
+// Workspace of siggate_forward_noalloc: a static device array, one copy on
+// every device the library runs on, held until the process ends.  In host
+// code `scratch` names a host-side stand-in, never a device address: the
+// device address comes from hipGetSymbolAddress, once per device, and only
+// that address is handed to kernels.
+static __device__ __align__(256) unsigned char scratch[SIGGATE_SCRATCH_BYTES];
+
+constexpr int MAX_DEVICES = 64;
+std::atomic<void *> scratch_ptr[MAX_DEVICES];
+std::mutex scratch_mutex;
+
+// The device address of `scratch` on the current device (looked up on the
+// first call on that device, with it current).
+hipError_t device_scratch(void **out)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= MAX_DEVICES) return hipErrorInvalidDevice;
+    void *p = scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(scratch_mutex);
+        p = scratch_ptr[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (e != hipSuccess) return e;
+            if (!p) return hipErrorInvalidSymbol;
+            scratch_ptr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return hipSuccess;
 }
 
 GateArgs gate_args(const void *x, const float *W, const float *bias, const siggate_cfg_t *c,
@@ -122,6 +159,18 @@ siggate_status_t siggate_forward(const void *x, const float *W, const float *bia
     return launch_gate(a, p, cfg->E, MODE_SELECT, (hipStream_t)stream) == hipSuccess
                ? SIGGATE_OK
                : SIGGATE_EHIP;
+}
+
+siggate_status_t siggate_forward_noalloc(const void *x, const float *W, const float *bias,
+                                         const siggate_cfg_t *cfg, float *weights,
+                                         int32_t *indices, void *stream)
+{
+    const siggate_status_t st = check_gate_cfg(cfg);
+    if (st != SIGGATE_OK) return st;
+    if (forward_bytes(cfg) > SIGGATE_SCRATCH_BYTES) return SIGGATE_ESCRATCH;
+    void *ws = nullptr;
+    if (device_scratch(&ws) != hipSuccess) return SIGGATE_EHIP;
+    return siggate_forward(x, W, bias, cfg, weights, indices, ws, SIGGATE_SCRATCH_BYTES, stream);
 }
 
 siggate_status_t siggate_logits(const void *x, const float *W, const siggate_cfg_t *cfg,
@@ -310,6 +359,9 @@ const char *siggate_status_str(siggate_status_t status)
     case SIGGATE_EUNSUPPORTED: return "SIGGATE_EUNSUPPORTED: configuration not built by this library";
     case SIGGATE_EWORKSPACE: return "SIGGATE_EWORKSPACE: workspace smaller than siggate_workspace_bytes";
     case SIGGATE_EHIP: return "SIGGATE_EHIP: HIP launch error";
+    case SIGGATE_ESCRATCH:
+        return "SIGGATE_ESCRATCH: the call needs more workspace than the static scratch "
+               "(SIGGATE_SCRATCH_BYTES)";
     default: return "unknown siggate status";
     }
 }

@@ -52,7 +52,7 @@ def test_exports_nothing_else(lib):
 
 
 def test_status_strings(lib):
-    for code in (0, -1, -2, -3, -4):
+    for code in (0, -1, -2, -3, -4, -5):
         assert sg.siggate_status_str(code).startswith("SIGGATE_")
     assert "unknown" in sg.siggate_status_str(7)
 
@@ -121,6 +121,37 @@ def test_forward_pointer_and_workspace_checks():
     assert call_forward(DSV3, ws=0) == binding.SIGGATE_EWORKSPACE
     # T = 0 enqueues nothing and needs no data pointers
     assert call_forward(DSV3.with_T(0), x=0, w=0, i=0, ws=0, ws_bytes=0) == binding.SIGGATE_OK
+
+
+def call_noalloc(cfg, x=FAKE, W=FAKE, bias=FAKE, w=FAKE, i=FAKE):
+    c = cfg.c()
+    return sg.load_library().siggate_forward_noalloc(x, W, bias, ctypes.byref(c), w, i, None)
+
+
+@pytest.mark.parametrize("bad", [dict(n_group=3), dict(top_k=0), dict(order=2), dict(T=-1),
+                                 dict(logits_path=2)])
+def test_noalloc_rejects_invalid(bad):
+    assert call_noalloc(sg.Cfg(**(DSV3.__dict__ | bad))) == binding.SIGGATE_EINVAL
+
+
+def test_noalloc_rejects_beyond_scratch():
+    """Checked on the host before the scratch is looked up or anything is
+    enqueued: an unsupported shape, then a workspace need above the scratch."""
+    assert call_noalloc(sg.Cfg(**(DSV3.__dict__ | dict(E=512, n_group=8)))) == \
+        binding.SIGGATE_EUNSUPPORTED
+    big = dataclasses.replace(KIMI.with_T(65536), logits_path=1)
+    assert sg.siggate_workspace_bytes(big) > binding.SIGGATE_SCRATCH_BYTES
+    assert call_noalloc(big) == binding.SIGGATE_ESCRATCH
+    # every batch of the float32 route fits
+    for T in (1, 256, 4096, 6144, 8191, 65536):
+        assert sg.siggate_workspace_bytes(KIMI.with_T(T)) <= binding.SIGGATE_SCRATCH_BYTES
+
+
+def test_scratch_size_matches_header():
+    with open(HEADER) as f:
+        text = f.read()
+    m = re.search(r"#define SIGGATE_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == binding.SIGGATE_SCRATCH_BYTES
 
 
 def test_dispatch_checks():
