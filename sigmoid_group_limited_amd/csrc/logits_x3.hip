@@ -127,16 +127,26 @@ __global__ __launch_bounds__(256) void x3_split_w_kernel(const float *W, uint16_
 // chunks are short, run a deeper ring instead).  At the end the k-half-1 wave
 // of each quarter hands its sums to the k-half-0 wave through LDS, which adds
 // them after its own (a fixed order) and writes the partial logits.
+// Every X3_FLUSH chunks, and at the end, the two k-half waves of a quarter
+// add their accumulators into one float32 total per element in LDS, k-half 0
+// first (a fixed order, the same at every flush for every token), and
+// restart them from zero; the k-half-0 wave writes the totals.
 template <int BM, int NBW>
 struct X3Wide {
     static constexpr int MB = BM / 16;               // token blocks per wave
     static constexpr int BN = 64 * NBW;              // experts per workgroup
     static constexpr int XQ = BM * 64 / 8 / 512;     // x pieces per thread per chunk
     static constexpr int STAGE = 2 * BM * 8;         // 16-byte slots: two x buffers
-    static constexpr int RED = 4 * MB * NBW * 64;    // 16-byte slots: k-split hand-over
-    static constexpr int SLOTS = STAGE > RED ? STAGE : RED;
+    static constexpr int TOT = 4 * MB * NBW * 64;    // 16-byte slots: float32 totals per quarter
+    static constexpr int SLOTS = STAGE + TOT;
     static_assert(XQ >= 1, "every thread stages whole x pieces");
 };
+
+// Blocked summation: every X3_FLUSH 64-column chunks the accumulators are
+// added into float32 totals in LDS and restarted from zero, so no rounding
+// chain spans more than X3_FLUSH chunks (3 MFMAs of 32 exact products each
+// per chunk); one chain over a k-half of d = 7168 would be 168 additions.
+constexpr int X3_FLUSH = 16;
 
 // 16-byte x pieces of one 128-byte row: 8 per row, permuted by the row so
 // that the 16 lanes of a fragment read (rows r..r+15, one piece) cover all
@@ -244,6 +254,38 @@ __global__ __launch_bounds__(512) void x3_gemm8_kernel(GateArgs a)
 #pragma unroll
         for (int n = 0; n < NBW; ++n) acc[m][n] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
+    // float32 totals of this quarter's tile in LDS, one 16-byte slot per
+    // accumulator and lane, shared by the quarter's two k-half waves
+    constexpr int REGS = MB * NBW;
+    f32x4 *const tot = (f32x4 *)(smem + S::STAGE) + wn * REGS * 64 + lane;
+    bool fresh = true;   // the totals hold nothing yet (the first flush stores)
+    auto flush = [&]() {
+        if (wk == 0) {
+#pragma unroll
+            for (int m = 0; m < MB; ++m)
+#pragma unroll
+                for (int n = 0; n < NBW; ++n) {
+                    f32x4 *const p = tot + (m * NBW + n) * 64;
+                    *p = fresh ? acc[m][n] : *p + acc[m][n];
+                    acc[m][n] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+                }
+        }
+        __syncthreads();
+        if (wk == 1) {
+#pragma unroll
+            for (int m = 0; m < MB; ++m)
+#pragma unroll
+                for (int n = 0; n < NBW; ++n) {
+                    f32x4 *const p = tot + (m * NBW + n) * 64;
+                    *p = *p + acc[m][n];
+                    acc[m][n] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+                }
+        }
+        __syncthreads();
+        fresh = false;
+    };
+    static_assert(X3_FLUSH % 4 == 0, "flushes fall between unrolled steps");
+
     constexpr int SG_MFMA = 0x008, SG_VMEM_READ = 0x020, SG_DS_READ = 0x100;
     if (npairs > 0) {
         if constexpr (SPLIT) {
@@ -293,6 +335,7 @@ __global__ __launch_bounds__(512) void x3_gemm8_kernel(GateArgs a)
             for (; j + PW <= npairs; j += PW) {
 #pragma unroll
                 for (int u = 0; u < PW; ++u) step(j + u, u);
+                if ((j + PW) % X3_FLUSH == 0) flush();
             }
 #pragma unroll
             for (int u = 0; u < PW - 1; ++u)
@@ -343,27 +386,20 @@ __global__ __launch_bounds__(512) void x3_gemm8_kernel(GateArgs a)
             for (; j + 2 <= npairs; j += 2) {
                 step(j, 0);
                 step(j + 1, 1);
+                if ((j + 2) % X3_FLUSH == 0) flush();
             }
             if (j < npairs) step(j, 0);
         }
     }
 
-    // k-split hand-over through LDS (the staging buffers are dead: the last
-    // step ended with a barrier), then the partial logits of the tile.
-    constexpr int REGS = MB * NBW;
-    u32x4 *const red = smem + wn * REGS * 64 + lane;
-    if (wk == 1) {
-#pragma unroll
-        for (int m = 0; m < MB; ++m)
-#pragma unroll
-            for (int n = 0; n < NBW; ++n) red[(m * NBW + n) * 64] = __builtin_bit_cast(u32x4, acc[m][n]);
-    }
-    __syncthreads();
+    // the last block into the totals (both k-halves, in order), then the
+    // k-half-0 wave writes the totals as the tile's partial logits
+    flush();
     if (wk == 1) return;
 #pragma unroll
     for (int m = 0; m < MB; ++m)
 #pragma unroll
-        for (int n = 0; n < NBW; ++n) acc[m][n] += __builtin_bit_cast(f32x4, red[(m * NBW + n) * 64]);
+        for (int n = 0; n < NBW; ++n) acc[m][n] = tot[(m * NBW + n) * 64];
     // accumulator r of block (m, n): token t0 + 16m + 4(l/16) + r, expert
     // e0 + 16(NBW*wn + n) + l%16
     float *const out = a.partial + (size_t)ks * a.T * a.E;

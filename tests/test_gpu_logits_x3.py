@@ -84,6 +84,10 @@ def test_x3_gate_parity_small(o, name, gc, T, d):
     say(f"    {stats}")
 
 
+# largest |v32 - v64| of the choice scores allowed: below the 1e-6 margin
+# under which a token is exempt, as on the float32 route
+SCORE_ERR_MAX = 1e-6
+
 # batch sizes across the route's plan at d=7168 (tile shape and k-slices)
 PLAN_SWEEP = [(2, 256), (33, 384), (65, 256), (129, 384), (300, 256), (511, 384),
               (1000, 256), (2047, 384), (4000, 256), (8191, 256), (12000, 384), (16384, 128)]
@@ -104,9 +108,13 @@ def test_x3_plan_sweep(o, T, E):
     rng = np.random.default_rng(T)
     rows = np.arange(T) if T <= 300 else np.unique(np.r_[0, 63, 64, 127, 128, T - 1,
                                                          rng.integers(0, T, 200)])
-    stats = compare_gate(w, i, oracle_gate(o, gi, cfg, rows), gc.route_scale, rows,
-                         topk_group=gc.topk_group)
+    ref = oracle_gate(o, gi, cfg, rows)
+    stats = compare_gate(w, i, ref, gc.route_scale, rows, topk_group=gc.topk_group)
+    lg = sg.siggate_logits(x, W, cfg).cpu().numpy()[rows]
+    stats.update(score_error(lg, o.logits(gi.x[rows], gi.W), gi.bias, ref.margins,
+                             np.all(i[rows] == ref.indices, axis=1)))
     say(f"    {stats}")
+    assert stats["score_max_abs_err"] < SCORE_ERR_MAX, stats
 
 
 @pytest.mark.parametrize("T,E,d", [(100, 256, 7168), (16384, 384, 96), (9000, 128, 40),
@@ -199,8 +207,9 @@ def test_x3_workload_full_size(o, name):
     s_all = compare_gate(w_np, i_np, sel, w.cfg.route_scale, topk_group=w.cfg.topk_group)
     stats["select_on_gpu_logits"] = {k: s_all[k] for k in ("tokens", "exempt", "index_mismatch_nonexempt",
                                                            "exempt_differ_valid", "weight_max_rel")}
-    # measured 1.1-1.3e-6 on this route's full-size batches
-    assert stats["score_max_abs_err"] < 2e-6, stats
+    # the exemption margin must stay above the float32 score error (one
+    # chain per k-half of d measured 1.1-1.3e-6 here; blocked summation less)
+    assert stats["score_max_abs_err"] < SCORE_ERR_MAX, stats
     if gi.twins:
         dec = np.zeros(len(rows), bool)
         for a, bb in gi.twins:
