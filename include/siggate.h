@@ -39,7 +39,7 @@
  *   - NaN or Inf in x, W or bias give undefined selections.
  *
  * Supported shapes (others return SIGGATE_EUNSUPPORTED):
- *   E in {128, 256, 384}; n_group a power of two with 1 <= n_group <= 64;
+ *   E in {128, 256, 384, 512}; n_group a power of two with 1 <= n_group <= 64;
  *   1 <= top_k <= 8; d a positive multiple of 8; 0 <= T <= 2^31 / top_k.
  * Invalid configurations return SIGGATE_EINVAL: topk_group outside
  * [1, n_group], top_k > topk_group * E / n_group, order not 0 or 1,
@@ -169,7 +169,9 @@ siggate_status_t siggate_forward_noalloc(const void *x, const float *W, const fl
  *                      perm (may be NULL)
  *   permuted_x         bfloat16 [T*top_k, d] out, row pos = x[perm[pos] / top_k]
  *   ws                 device workspace (see siggate_forward)
- * Only T, d, E and top_k of cfg are used. */
+ * Only T, d, E and top_k of cfg are used: 1 <= top_k <= 8, top_k <= E <= 512,
+ * d a positive multiple of 8 (others return SIGGATE_EUNSUPPORTED or
+ * SIGGATE_EINVAL). */
 siggate_status_t siggate_dispatch(const void *x, const int32_t *indices,
                                   const siggate_cfg_t *cfg,
                                   int32_t *tokens_per_expert, int32_t *offsets,
@@ -225,7 +227,7 @@ siggate_status_t siggate_ep_regroup(const int32_t *counts, int32_t ep_size, int3
  *   pair_slot     int32 [T * top_k]    out, position in send_tokens of
  *                 (t, rank of the k-th expert of t)
  *   ws            siggate_ep_workspace_bytes(cfg, ep_size) bytes
- * ep_size <= 384. */
+ * ep_size <= 512. */
 size_t siggate_ep_workspace_bytes(const siggate_cfg_t *cfg, int32_t ep_size);
 siggate_status_t siggate_ep_dedup(const int32_t *indices, const siggate_cfg_t *cfg,
                                   int32_t ep_size, int32_t *rank_counts,

@@ -8,20 +8,22 @@
 //          this is one of its valid results)
 //   permuted_x[pos] = x[perm[pos] / K]
 //
-// Four launches (one for small batches, below), none of them with
+// Three launches (one for small batches, below), none of them with
 // order-dependent atomics:
 //   count   one block per 256 tokens; each wave ORs a 64-bit lane mask per
 //           expert in LDS (bit l = token l of the wave routes there), so the
-//           block's count of expert e is the popcount of its 4 masks;
-//           written expert-major, counts[e][b].
-//   scan    one block per expert: exclusive prefix of counts[e][.] over
-//           the token blocks, and the expert's total.
-//   scatter each block takes the exclusive prefix of the E totals (the
-//           expert offsets), recomputes its masks, and places every pair at
-//           offset[e] + prefix[e][b] + (popcount of lower lanes' bits plus
-//           earlier waves' counts) -- exactly ascending token order.
-//   gather  one block per token: read the row once, write it to its K
-//           destinations with non-temporal 16-byte stores.
+//           block's count of expert e is the popcount of its 4 masks, and a
+//           pair's rank among the block's pairs of its expert -- popcount of
+//           the lower lanes' bits plus the earlier waves' counts -- is
+//           exactly its rank in ascending token order (stable).  Writes the
+//           counts block-major, counts[b][e], and the ranks into dest.
+//   scan    one block: per expert, the total over token blocks and the
+//           exclusive prefix over them; the exclusive prefix of the totals
+//           over experts (the expert offsets); base[b][e] = offset[e] +
+//           prefix[e][b]; tokens_per_expert and offsets.
+//   gather  one block per token: each pair lands at base[b][e] + rank (its
+//           block writes dest and perm), then the row is read once and
+//           written to its K destinations with non-temporal 16-byte stores.
 #include "siggate_internal.h"
 
 namespace siggate {
@@ -32,7 +34,6 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int BT = DISPATCH_BLOCK_TOKENS;
 constexpr int WAVES = BT / 64;
-constexpr int SCAN_THREADS = 256;
 
 // Loads the K expert ids of token t into e[] (-1 past K or for t >= T).
 __device__ __forceinline__ void load_row(const DispatchArgs &a, int t, int (&e)[MAX_TOPK])
@@ -71,121 +72,191 @@ __global__ __launch_bounds__(BT) void dispatch_count_kernel(DispatchArgs a)
 {
     __shared__ unsigned long long masks[WAVES][MAX_EXPERTS];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int t = blockIdx.x * BT + threadIdx.x;
     int e[MAX_TOPK];
-    load_row(a, blockIdx.x * BT + threadIdx.x, e);
+    load_row(a, t, e);
     build_masks(a, masks, e, lane, wave);
+    int32_t *const cnt = a.block_counts + (size_t)blockIdx.x * a.E;
     for (int x = threadIdx.x; x < a.E; x += BT) {
         int c = 0;
 #pragma unroll
         for (int w = 0; w < WAVES; ++w) c += __popcll(masks[w][x]);
-        a.block_counts[(size_t)x * a.n_blocks + blockIdx.x] = c;
+        cnt[x] = c;
+    }
+    // rank of each of this token's pairs among the block's pairs of its
+    // expert, in token order; -1 for an id out of range
+    if (t >= a.T) return;
+    const unsigned long long lower = (1ull << lane) - 1ull;
+    int r[MAX_TOPK];
+#pragma unroll
+    for (int k = 0; k < MAX_TOPK; ++k) {
+        const int x = e[k];
+        r[k] = -1;
+        if (k < a.top_k && (unsigned)x < (unsigned)a.E) {
+            r[k] = __popcll(masks[wave][x] & lower);
+            for (int w = 0; w < wave; ++w) r[k] += __popcll(masks[w][x]);
+        }
+    }
+    int32_t *const out = a.dest + (size_t)t * a.top_k;
+    if (a.top_k == 8) {
+        *(i32x4 *)out = i32x4{r[0], r[1], r[2], r[3]};
+        *(i32x4 *)(out + 4) = i32x4{r[4], r[5], r[6], r[7]};
+    } else {
+#pragma unroll
+        for (int k = 0; k < MAX_TOPK; ++k)
+            if (k < a.top_k) out[k] = r[k];
     }
 }
 
-// Block e: exclusive prefix over token blocks of counts[e][.] (in place
-// into block_base[e][.]) and tokens_per_expert[e].
-__global__ __launch_bounds__(SCAN_THREADS) void dispatch_scan_kernel(DispatchArgs a)
+// One block.  Thread (part, e) owns expert e and the part-th run of token
+// blocks: it sums their counts (CB loads in flight at a time), the parts'
+// sums give the expert's total and each part's starting prefix, a block-wide
+// scan of the totals gives the expert offsets, and a second pass over the
+// run writes base[b][e] = offset[e] + (counts of e in blocks before b).
+constexpr int SCAN_NT = 1024;
+constexpr int SCAN_CB = 32;
+
+__global__ __launch_bounds__(SCAN_NT) void dispatch_scan_kernel(DispatchArgs a)
 {
-    __shared__ int wave_tot[SCAN_THREADS / 64];
-    const int e = blockIdx.x;
-    const int NB = a.n_blocks;
+    __shared__ int part_tot[SCAN_NT];       // [part][e]
+    __shared__ int wave_tot[SCAN_NT / 64];
+    __shared__ int exp_off[MAX_EXPERTS];
+    const int E = a.E, NB = a.n_blocks;
+    int parts = 1;
+    while (parts * 2 * E <= SCAN_NT) parts *= 2;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int32_t *cnt = a.block_counts + (size_t)e * NB;
-    int32_t *base = a.block_base + (size_t)e * NB;
-    int carry = 0;
-    for (int b0 = 0; b0 < NB; b0 += SCAN_THREADS) {
-        const int b = b0 + tid;
-        const int c = b < NB ? cnt[b] : 0;
-        int inc = c;
-        for (int off = 1; off < 64; off <<= 1) {
-            const int y = __shfl_up(inc, off);
-            if (lane >= off) inc += y;
-        }
-        if (lane == 63) wave_tot[wave] = inc;
-        __syncthreads();
-        int before = 0, all = 0;
-        for (int w = 0; w < SCAN_THREADS / 64; ++w) {
-            before += w < wave ? wave_tot[w] : 0;
-            all += wave_tot[w];
-        }
-        if (b < NB) base[b] = carry + before + inc - c;
-        carry += all;
-        __syncthreads();
-    }
-    if (tid == 0) a.tokens_per_expert[e] = carry;
-}
+    const int part = tid / E, e = tid - part * E;
+    const bool live = part < parts;
+    const int run = (NB + parts - 1) / parts;
+    const int b_begin = live ? min(part * run, NB) : NB;
+    const int b_end = live ? min(b_begin + run, NB) : NB;
+    const int32_t *const cnt = a.block_counts;
 
-__global__ __launch_bounds__(BT) void dispatch_scatter_kernel(DispatchArgs a)
-{
-    __shared__ unsigned long long masks[WAVES][MAX_EXPERTS];
-    __shared__ int offset[MAX_EXPERTS];
-    __shared__ int wave_tot[WAVES];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int t = blockIdx.x * BT + threadIdx.x;
-
-    // Expert offsets: exclusive prefix of tokens_per_expert over experts.
-    for (int e0 = 0; e0 < a.E; e0 += BT) {
-        const int x = e0 + threadIdx.x;
-        const int c = x < a.E ? a.tokens_per_expert[x] : 0;
-        int inc = c;
-        for (int off = 1; off < 64; off <<= 1) {
-            const int y = __shfl_up(inc, off);
-            if (lane >= off) inc += y;
-        }
-        if (lane == 63) wave_tot[wave] = inc;
-        __syncthreads();
-        int before = e0 > 0 ? offset[e0 - 1] : 0;   // inclusive total so far
-        for (int w = 0; w < wave; ++w) before += wave_tot[w];
-        __syncthreads();
-        if (x < a.E) offset[x] = before + inc;        // inclusive for now
-        __syncthreads();
+    // a run of at most SCAN_CB blocks (T <= 16384 * parts) stays in
+    // registers for the second pass; longer runs are read again
+    const bool one = b_end - b_begin <= SCAN_CB;
+    int v[SCAN_CB];
+    int sum = 0;
+    for (int b0 = b_begin; b0 < b_end; b0 += SCAN_CB) {
+#pragma unroll
+        for (int u = 0; u < SCAN_CB; ++u) v[u] = b0 + u < b_end ? cnt[(size_t)(b0 + u) * E + e] : 0;
+#pragma unroll
+        for (int u = 0; u < SCAN_CB; ++u) sum += v[u];
     }
-    for (int x = threadIdx.x; x < a.E; x += BT) {
-        const int excl = offset[x] - a.tokens_per_expert[x];
-        if (blockIdx.x == 0 && a.offsets) {
-            a.offsets[x] = excl;
-            if (x == a.E - 1) a.offsets[a.E] = offset[x];
+    if (live) part_tot[part * E + e] = sum;
+    __syncthreads();
+    // expert totals (parts in order) and this part's start inside its expert
+    int total = 0, start = 0;
+    if (live) {
+        for (int q = 0; q < parts; ++q) {
+            const int c = part_tot[q * E + e];
+            start += q < part ? c : 0;
+            total += c;
+        }
+    }
+    // exclusive scan of the totals over experts: the part-0 threads carry
+    // experts 0 .. E-1 in thread order
+    const int tv = (live && part == 0) ? total : 0;
+    int inc = tv;
+    for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(inc, off);
+        if (lane >= off) inc += y;
+    }
+    if (lane == 63) wave_tot[wave] = inc;
+    __syncthreads();
+    int before = 0;
+    for (int w = 0; w < wave; ++w) before += wave_tot[w];
+    if (live && part == 0) {
+        exp_off[e] = before + inc - tv;
+        a.tokens_per_expert[e] = total;
+        if (a.offsets) {
+            a.offsets[e] = before + inc - tv;
+            if (e == E - 1) a.offsets[E] = before + inc;
         }
     }
     __syncthreads();
-    for (int x = threadIdx.x; x < a.E; x += BT)
-        offset[x] -= a.tokens_per_expert[x];   // now exclusive
-
-    int e[MAX_TOPK];
-    load_row(a, t, e);
-    build_masks(a, masks, e, lane, wave);   // its barriers also publish offset[]
-    if (t >= a.T) return;
-    const unsigned long long lower = (1ull << lane) - 1ull;
+    if (!live) return;
+    int acc = exp_off[e] + start;
+    for (int b0 = b_begin; b0 < b_end; b0 += SCAN_CB) {
+        if (!one) {
 #pragma unroll
-    for (int k = 0; k < MAX_TOPK; ++k) {
-        if (k >= a.top_k) break;
-        const size_t p = (size_t)t * a.top_k + k;
-        const int x = e[k];
-        if ((unsigned)x >= (unsigned)a.E) {
-            a.dest[p] = -1;
-            continue;
+            for (int u = 0; u < SCAN_CB; ++u) v[u] = b0 + u < b_end ? cnt[(size_t)(b0 + u) * E + e] : 0;
         }
-        int pos = offset[x] + a.block_base[(size_t)x * a.n_blocks + blockIdx.x] +
-                  __popcll(masks[wave][x] & lower);
-        for (int w = 0; w < wave; ++w) pos += __popcll(masks[w][x]);
-        a.perm[pos] = (int)p;
-        a.dest[p] = pos;
+#pragma unroll
+        for (int u = 0; u < SCAN_CB; ++u) {
+            if (b0 + u < b_end) a.block_base[(size_t)(b0 + u) * E + e] = acc;
+            acc += v[u];
+        }
     }
 }
 
-__global__ __launch_bounds__(256) void dispatch_gather_kernel(DispatchArgs a)
+// Final position of pair p = t*K + k: base[t / BT][e] + its rank (held in
+// dest on entry); -1 for an id out of range.
+__device__ __forceinline__ int final_pos(const DispatchArgs &a, int t, int k)
+{
+    const size_t p = (size_t)t * a.top_k + k;
+    const int x = a.indices[p];
+    const int r = a.dest[p];
+    return ((unsigned)x < (unsigned)a.E && r >= 0)
+               ? a.block_base[(size_t)(t / BT) * a.E + x] + r : -1;
+}
+
+// Positions without rows (the expert-parallel de-duplication): one thread
+// per pair writes dest and perm.
+__global__ __launch_bounds__(256) void dispatch_place_kernel(DispatchArgs a)
+{
+    const long p = (long)blockIdx.x * 256 + threadIdx.x;
+    if (p >= (long)a.T * a.top_k) return;
+    const int t = (int)(p / a.top_k), k = (int)(p - (long)t * a.top_k);
+    const int pos = final_pos(a, t, k);
+    if (pos >= 0) a.perm[pos] = (int)p;
+    a.dest[p] = pos;
+}
+
+// One block per token: the pairs' final positions (written to dest and
+// perm by the first top_k threads), then the row, read once, to its K
+// destinations.  The first loads of the row are issued before the
+// positions are known, so their latency overlaps the index loads.
+constexpr int GATHER_NT = 256;
+constexpr int GATHER_PF = 2;   // 16-byte pieces per thread loaded up front
+
+__global__ __launch_bounds__(GATHER_NT) void dispatch_gather_kernel(DispatchArgs a)
 {
     const int t = blockIdx.x;
-    const long npos = (long)a.T * a.top_k;
-    int dst[MAX_TOPK];
-#pragma unroll
-    for (int k = 0; k < MAX_TOPK; ++k) {
-        const int v = k < a.top_k ? a.dest[(size_t)t * a.top_k + k] : -1;
-        dst[k] = (v >= 0 && v < npos) ? v : -1;
-    }
     const int nvec = a.d / 8;
     const u32x4 *src = (const u32x4 *)(a.x + (size_t)t * a.d);
-    for (int i = threadIdx.x; i < nvec; i += blockDim.x) {
+    u32x4 pf[GATHER_PF] = {};
+#pragma unroll
+    for (int j = 0; j < GATHER_PF; ++j) {
+        const int i = threadIdx.x + j * GATHER_NT;
+        if (i < nvec) pf[j] = src[i];
+    }
+    int dst[MAX_TOPK];
+#pragma unroll
+    for (int k = 0; k < MAX_TOPK; ++k) dst[k] = k < a.top_k ? final_pos(a, t, k) : -1;
+    // every thread has read its dest entries above before any is rewritten
+    __syncthreads();
+    if (threadIdx.x < a.top_k) {
+        const int k = threadIdx.x;
+        const size_t p = (size_t)t * a.top_k + k;
+        int pos = -1;
+#pragma unroll
+        for (int j = 0; j < MAX_TOPK; ++j)
+            if (j == k) pos = dst[j];
+        if (pos >= 0) a.perm[pos] = (int)p;
+        a.dest[p] = pos;
+    }
+#pragma unroll
+    for (int j = 0; j < GATHER_PF; ++j) {
+        const int i = threadIdx.x + j * GATHER_NT;
+        if (i < nvec) {
+#pragma unroll
+            for (int k = 0; k < MAX_TOPK; ++k)
+                if (dst[k] >= 0)
+                    __builtin_nontemporal_store(pf[j], (u32x4 *)(a.permuted_x + (size_t)dst[k] * a.d) + i);
+        }
+    }
+    for (int i = threadIdx.x + GATHER_PF * GATHER_NT; i < nvec; i += GATHER_NT) {
         const u32x4 val = src[i];
 #pragma unroll
         for (int k = 0; k < MAX_TOPK; ++k)
@@ -335,12 +406,21 @@ size_t dispatch_workspace_bytes(int T, int E, int top_k, bool need_dest)
     return bytes;
 }
 
+// count and scan: the ranks in dest, the base table, tokens_per_expert, offsets
+static hipError_t launch_count_scan(const DispatchArgs &a, hipStream_t stream)
+{
+    hipError_t e = launch_kernel(dispatch_count_kernel, dim3(a.n_blocks), dim3(BT), stream, a);
+    if (e == hipSuccess) e = launch_kernel(dispatch_scan_kernel, dim3(1), dim3(SCAN_NT), stream, a);
+    return e;
+}
+
 hipError_t launch_dispatch_meta(const DispatchArgs &a, hipStream_t stream)
 {
     if (a.n_blocks == 0) return launch_kernel(dispatch_zero_kernel, dim3(1), dim3(BT), stream, a);
-    hipError_t e = launch_kernel(dispatch_count_kernel, dim3(a.n_blocks), dim3(BT), stream, a);
-    if (e == hipSuccess) e = launch_kernel(dispatch_scan_kernel, dim3(a.E), dim3(SCAN_THREADS), stream, a);
-    if (e == hipSuccess) e = launch_kernel(dispatch_scatter_kernel, dim3(a.n_blocks), dim3(BT), stream, a);
+    hipError_t e = launch_count_scan(a, stream);
+    const long pairs = (long)a.T * a.top_k;
+    if (e == hipSuccess)
+        e = launch_kernel(dispatch_place_kernel, dim3((unsigned)((pairs + 255) / 256)), dim3(256), stream, a);
     return e;
 }
 
@@ -354,8 +434,8 @@ hipError_t launch_dispatch(const DispatchArgs &a, hipStream_t stream)
         return launch_kernel(dispatch_small_kernel, dim3(a.T * parts), dim3(SMALL_NT), stream, a,
                              parts);
     }
-    hipError_t e = launch_dispatch_meta(a, stream);
-    if (e == hipSuccess) e = launch_kernel(dispatch_gather_kernel, dim3(a.T), dim3(256), stream, a);
+    hipError_t e = launch_count_scan(a, stream);
+    if (e == hipSuccess) e = launch_kernel(dispatch_gather_kernel, dim3(a.T), dim3(GATHER_NT), stream, a);
     return e;
 }
 

@@ -777,6 +777,11 @@ __global__ __launch_bounds__(64 * NWR) void gate_reduce_kernel(GateArgs a)
     finish_reduce<V, MODE>(a, lg, lane, t, scratch);
 }
 
+// Largest E with 64-token fused tiles: their double-buffered stage of W and x,
+// 2*(E + 64)*KPAD floats, exceeds the 160 KB of LDS at E = 512 (162 KB),
+// where the fused path uses 32-token tiles only.
+constexpr int MAX_E_TILE64 = 384;
+
 template <int E>
 hipError_t launch_for_e(const GateArgs &a, const GatePlan &p, GateMode final_mode,
                         hipStream_t stream)
@@ -786,11 +791,15 @@ hipError_t launch_for_e(const GateArgs &a, const GatePlan &p, GateMode final_mod
         // 64 tokens: 8 waves, two per SIMD; 32 tokens: 8 waves, the two of a
         // pair split every chunk's k
         const dim3 grid(p.grid), block(64 * 8);
-        if (p.m_blocks == 2)
-            return sel ? launch_kernel(gate_gemm_kernel<E, 2, 8, MODE_SELECT, 2, true>, grid, block, stream, a)
-                       : launch_kernel(gate_gemm_kernel<E, 2, 8, MODE_LOGITS, 2, true>, grid, block, stream, a);
-        return sel ? launch_kernel(gate_gemm_kernel<E, 1, 8, MODE_SELECT, 2, true>, grid, block, stream, a)
-                   : launch_kernel(gate_gemm_kernel<E, 1, 8, MODE_LOGITS, 2, true>, grid, block, stream, a);
+        if constexpr (E <= MAX_E_TILE64) {
+            if (p.m_blocks == 2)
+                return sel ? launch_kernel(gate_gemm_kernel<E, 2, 8, MODE_SELECT, 2, true>, grid, block, stream, a)
+                           : launch_kernel(gate_gemm_kernel<E, 2, 8, MODE_LOGITS, 2, true>, grid, block, stream, a);
+        }
+        // one register stage of loads ahead at E = 512, where two would spill
+        constexpr int P1 = E > MAX_E_TILE64 ? 1 : 2;
+        return sel ? launch_kernel(gate_gemm_kernel<E, 1, 8, MODE_SELECT, P1, true>, grid, block, stream, a)
+                   : launch_kernel(gate_gemm_kernel<E, 1, 8, MODE_LOGITS, P1, true>, grid, block, stream, a);
     }
     // split GEMM: 32 tokens x 128 experts, 8 waves (two per SIMD): 4 columns
     // of 32 experts x 2 k-halves of every chunk; or the bfloat16 three-way
@@ -806,13 +815,16 @@ hipError_t launch_for_e(const GateArgs &a, const GatePlan &p, GateMode final_mod
                           dim3(p.grid), dim3(64 * 8), stream, a);
     if (e != hipSuccess) return e;
     // few slices: one wave per token loads them all at once; more: 16 waves
-    // per token, each loading a contiguous run of them
+    // per token (8 at E = 512, whose selection needs more than the 128
+    // registers a 16-wave workgroup leaves a wave), each loading a
+    // contiguous run of them
     const dim3 rgrid(a.T);
     if (p.n_split <= ONE_WAVE_SLICES)
         return sel ? launch_kernel(gate_reduce_kernel<E, MODE_SELECT, 1>, rgrid, dim3(64), stream, a)
                    : launch_kernel(gate_reduce_kernel<E, MODE_LOGITS, 1>, rgrid, dim3(64), stream, a);
-    return sel ? launch_kernel(gate_reduce_kernel<E, MODE_SELECT, 16>, rgrid, dim3(1024), stream, a)
-               : launch_kernel(gate_reduce_kernel<E, MODE_LOGITS, 16>, rgrid, dim3(1024), stream, a);
+    constexpr int NWR = E > MAX_E_TILE64 ? 8 : 16;
+    return sel ? launch_kernel(gate_reduce_kernel<E, MODE_SELECT, NWR>, rgrid, dim3(64 * NWR), stream, a)
+               : launch_kernel(gate_reduce_kernel<E, MODE_LOGITS, NWR>, rgrid, dim3(64 * NWR), stream, a);
 }
 
 }  // namespace
@@ -847,7 +859,7 @@ GatePlan plan_gate(int T, int d, int E, int path)
     // ones, and a partly filled last round costs a whole one.
     if (tiles64 >= N_CU || tiles32 >= N_CU) {
         const long r64 = (tiles64 + N_CU - 1) / N_CU, r32 = (tiles32 + N_CU - 1) / N_CU;
-        p.m_blocks = (double)r64 * FUSED_ROUND_RATIO < (double)r32 ? 2 : 1;
+        p.m_blocks = E <= MAX_E_TILE64 && (double)r64 * FUSED_ROUND_RATIO < (double)r32 ? 2 : 1;
         p.t_tiles = (int)(p.m_blocks == 2 ? tiles64 : tiles32);
         p.grid = p.t_tiles;
         return p;
@@ -884,6 +896,7 @@ hipError_t launch_gate(const GateArgs &a, const GatePlan &p, int E, GateMode fin
     case 128: return launch_for_e<128>(a, p, final_mode, stream);
     case 256: return launch_for_e<256>(a, p, final_mode, stream);
     case 384: return launch_for_e<384>(a, p, final_mode, stream);
+    case 512: return launch_for_e<512>(a, p, final_mode, stream);
     default: return hipErrorInvalidValue;
     }
 }

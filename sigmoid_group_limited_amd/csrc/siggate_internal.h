@@ -26,7 +26,7 @@ constexpr int KC = 32;
 // tokens per dispatch block (4 waves of 64 lanes, one token per lane)
 constexpr int DISPATCH_BLOCK_TOKENS = 256;
 // largest expert count any kernel instantiates
-constexpr int MAX_EXPERTS = 384;
+constexpr int MAX_EXPERTS = 512;
 // largest top_k
 constexpr int MAX_TOPK = 8;
 

@@ -101,7 +101,7 @@ def test_forward_rejects_invalid(bad):
 
 
 @pytest.mark.parametrize("unsup", [
-    dict(E=64, n_group=8), dict(E=512, n_group=8), dict(E=192, n_group=8),
+    dict(E=64, n_group=8), dict(E=640, n_group=8), dict(E=192, n_group=8),
     dict(n_group=128, topk_group=4, top_k=4), dict(top_k=9, topk_group=8, n_group=8),
     dict(d=7164),
 ])
@@ -137,7 +137,7 @@ def test_noalloc_rejects_invalid(bad):
 def test_noalloc_rejects_beyond_scratch():
     """Checked on the host before the scratch is looked up or anything is
     enqueued: an unsupported shape, then a workspace need above the scratch."""
-    assert call_noalloc(sg.Cfg(**(DSV3.__dict__ | dict(E=512, n_group=8)))) == \
+    assert call_noalloc(sg.Cfg(**(DSV3.__dict__ | dict(E=640, n_group=8)))) == \
         binding.SIGGATE_EUNSUPPORTED
     big = dataclasses.replace(KIMI.with_T(65536), logits_path=1)
     assert sg.siggate_workspace_bytes(big) > binding.SIGGATE_SCRATCH_BYTES
@@ -156,7 +156,7 @@ def test_scratch_size_matches_header():
 
 def test_dispatch_checks():
     cfg = DSV3.with_T(1000)
-    assert call_dispatch(cfg.__class__(**(cfg.__dict__ | dict(E=385)))) == \
+    assert call_dispatch(cfg.__class__(**(cfg.__dict__ | dict(E=513)))) == \
         binding.SIGGATE_EUNSUPPORTED
     assert call_dispatch(cfg.__class__(**(cfg.__dict__ | dict(top_k=9, E=300)))) == \
         binding.SIGGATE_EUNSUPPORTED

@@ -67,6 +67,8 @@ SMALL = [
     ("dsv3_T16447_d200", wl.DSV3, 16447, 200),
     ("e128_g4_T16400_d96", wl.GateConfig(128, 4, 2, 6, 1.0), 16400, 96),
     ("e128_g64_kg4_k8_all_kept_T300_d512", wl.GateConfig(128, 64, 4, 8, 1.0), 300, 512),
+    ("e512_g8_T200_d7168", wl.GateConfig(512, 8, 4, 8, 2.5), 200, 7168),
+    ("e512_g1_T2100_d1000", wl.GateConfig(512, 1, 1, 8, 2.827), 2100, 1000),
 ]
 
 
@@ -90,12 +92,14 @@ SCORE_ERR_MAX = 1e-6
 
 # batch sizes across the route's plan at d=7168 (tile shape and k-slices)
 PLAN_SWEEP = [(2, 256), (33, 384), (65, 256), (129, 384), (300, 256), (511, 384),
-              (1000, 256), (2047, 384), (4000, 256), (8191, 256), (12000, 384), (16384, 128)]
+              (1000, 256), (2047, 384), (4000, 256), (8191, 256), (12000, 384), (16384, 128),
+              (256, 512), (5000, 512)]
 
 
 @pytest.mark.parametrize("T,E", PLAN_SWEEP, ids=[f"T{t}_E{e}" for t, e in PLAN_SWEEP])
 def test_x3_plan_sweep(o, T, E):
-    gc = {128: wl.GateConfig(128, 4, 2, 6, 1.0), 256: wl.DSV3, 384: wl.KIMI_K2}[E]
+    gc = {128: wl.GateConfig(128, 4, 2, 6, 1.0), 256: wl.DSV3, 384: wl.KIMI_K2,
+          512: wl.GateConfig(512, 8, 4, 8, 2.5)}[E]
     d = 7168
     say(f"[x3 plan] T={T} E={E}")
     gi = wl.make_gate_inputs(T, d, gc, seed=T * 7 + E)

@@ -80,6 +80,11 @@ SMALL = [
     # every group kept (the group stage selects nothing away)
     ("e256_g8_kg8_T200_d1024", wl.GateConfig(256, 8, 8, 8, 2.5), 200, 1024),
     ("e128_g1_fused32_T20000_d136", wl.GateConfig(128, 1, 1, 8, 2.5), 20000, 136),
+    # 512 experts: split tiles of 4 expert tiles, fused tiles of 32 tokens only
+    ("e512_g8_T300_d7168", wl.GateConfig(512, 8, 4, 8, 2.5), 300, 7168),
+    ("e512_g1_T77_d1000", wl.GateConfig(512, 1, 1, 8, 2.827), 77, 1000),
+    ("e512_g16_fused32_T9000_d264", wl.GateConfig(512, 16, 4, 8, 2.5), 9000, 264),
+    ("e512_g64_fused32_T16500_d96", wl.GateConfig(512, 64, 8, 6, 1.0), 16500, 96),
 ]
 
 
@@ -122,14 +127,14 @@ def test_gate_parity_small(o, name, gc, T, d, order):
 # multiple of 8, ragged last token tiles; and both fused tile heights.
 PLAN_SWEEP = [(2, 256), (33, 384), (65, 256), (129, 384), (300, 256), (511, 384),
               (1000, 256), (2047, 384), (4000, 256), (6000, 384), (8191, 256), (12000, 384),
-              (20000, 384)]
+              (20000, 384), (256, 512), (3000, 512), (10000, 512)]
 
 
 @pytest.mark.parametrize("T,E", PLAN_SWEEP, ids=[f"T{t}_E{e}" for t, e in PLAN_SWEEP])
 def test_gate_plan_sweep(o, T, E):
     """Full-width d over the batch sizes where the GEMM plan changes; the
     oracle on sampled tokens (first, last and random), properties on all."""
-    gc = wl.DSV3 if E == 256 else wl.KIMI_K2
+    gc = {256: wl.DSV3, 384: wl.KIMI_K2, 512: wl.GateConfig(512, 8, 4, 8, 2.5)}[E]
     d = 7168
     say(f"[plan] T={T} E={E}")
     gi = wl.make_gate_inputs(T, d, gc, seed=T * 7 + E)
@@ -152,7 +157,8 @@ def test_gate_plan_sweep(o, T, E):
     (100, 256, 7168), (16384, 384, 96), (9000, 128, 40),
     # full d with blocked summation: fused 64- and 32-token tiles flushing
     # every 16 chunks, and split tiles with long k-slices (1 and 5 slices)
-    (16384, 384, 7168), (20480, 256, 7168), (4096, 256, 7168), (512, 384, 7168)])
+    (16384, 384, 7168), (20480, 256, 7168), (4096, 256, 7168), (512, 384, 7168),
+    (9000, 512, 7168), (256, 512, 7168)])
 def test_logits_exact_on_integer_inputs(o, T, E, d):
     """x small integers, W integers times 2^-8: every partial sum is exact in
     float32, so GPU logits equal the oracle's bit for bit on both the split

@@ -21,13 +21,15 @@ CHILD = textwrap.dedent("""
     from sigmoid_group_limited_amd import workloads as wl
     o = oracle.Oracle(LIB)
     for gc, T, d in [(wl.DSV3, 37, 64), (wl.KIMI_K2, 20, 40), (wl.GateConfig(128, 64, 4, 8, 1.0), 9, 24),
-                     (wl.DSV3, 1, 8)]:
+                     (wl.DSV3, 1, 8), (wl.GateConfig(512, 8, 4, 8, 2.5), 5, 16)]:
         gi = wl.make_gate_inputs(T, d, gc, seed=T)
         for opts in ({}, {"score_func": 1}, {"mask_zero": 1, "denom_eps": 1e-20}, {"renorm": 2}):
             for bias in (gi.bias, None):
                 r = o.gate(gi.x, gi.W, bias, gc.n_group, gc.topk_group, gc.top_k, gc.route_scale,
                            order=1, **opts)
-        r = o.gate(gi.x, gi.W, gi.bias, gc.n_group, gc.topk_group, gc.top_k, gc.route_scale)
+        r = o.gate(gi.x, gi.W, gi.bias, gc.n_group, gc.topk_group, gc.top_k, gc.route_scale,
+                   with_scores=True)
+        o.scores(o.logits(gi.x, gi.W), None, gc.n_group, score_func=1)
         dr = o.dispatch(r.indices, gc.n_experts)
         o.gather_rows(gi.x, dr.perm, gc.top_k)
         outs = wl.bf16_bits(np.random.default_rng(1).standard_normal((T * gc.top_k, d), dtype=np.float32))
