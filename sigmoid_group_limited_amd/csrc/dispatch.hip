@@ -114,7 +114,7 @@ __global__ __launch_bounds__(BT) void dispatch_count_kernel(DispatchArgs a)
 // scan of the totals gives the expert offsets, and a second pass over the
 // run writes base[b][e] = offset[e] + (counts of e in blocks before b).
 constexpr int SCAN_NT = 1024;
-constexpr int SCAN_CB = 32;
+constexpr int SCAN_CB = 64;
 
 __global__ __launch_bounds__(SCAN_NT) void dispatch_scan_kernel(DispatchArgs a)
 {
@@ -132,7 +132,7 @@ __global__ __launch_bounds__(SCAN_NT) void dispatch_scan_kernel(DispatchArgs a)
     const int b_end = live ? min(b_begin + run, NB) : NB;
     const int32_t *const cnt = a.block_counts;
 
-    // a run of at most SCAN_CB blocks (T <= 16384 * parts) stays in
+    // a run of at most SCAN_CB blocks (T <= 16384 * parts at SCAN_CB = 64) stays in
     // registers for the second pass; longer runs are read again
     const bool one = b_end - b_begin <= SCAN_CB;
     int v[SCAN_CB];
