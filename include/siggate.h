@@ -23,9 +23,11 @@
  *        permuted_x[pos] = x[perm[pos] / top_k].
  *
  * Conventions shared by every call
- *   - All array arguments are DEVICE pointers owned by the caller; the
- *     library allocates nothing, keeps no state between calls and is
- *     reentrant.  Every pointer must be 16-byte aligned.
+ *   - All array arguments are DEVICE pointers owned by the caller; no call
+ *     allocates device memory.  Every call except siggate_forward_noalloc
+ *     keeps no state between calls and is reentrant (that one shares a
+ *     static device scratch, see its declaration).  Every pointer must be
+ *     16-byte aligned.
  *   - All arrays are dense row-major.
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the default
  *     stream) and runs asynchronously; there is no host synchronisation.
