@@ -1,5 +1,6 @@
 // api.hip -- the C ABI of libsiggate (declared in include/siggate.h):
-// argument checks, workspace layout and kernel launches.  Host code only.
+// argument checks, workspace layout and kernel launches (host code), and
+// the static device scratch of siggate_forward_noalloc.
 #include <string.h>
 
 #include <atomic>

@@ -183,7 +183,7 @@ def test_x3_logits_tolerance(o, name):
 
 @pytest.mark.parametrize("name", list(wl.WORKLOADS))
 def test_x3_workload_full_size(o, name):
-    """Full-size workload on the bfloat16 three-way route: sampled tokens
+    """Full-size workload on the bfloat16 three-way route: every token
     against the oracle, row properties everywhere, exact twin ties, and the
     dispatch of the route's indices."""
     w = wl.WORKLOADS[name]
@@ -195,14 +195,15 @@ def test_x3_workload_full_size(o, name):
     torch.cuda.synchronize()
     w_np, i_np = wg.cpu().numpy(), ig.cpu().numpy()
     check_rows_valid(i_np, w.cfg.n_experts, w.cfg.n_group, w.cfg.topk_group)
-    rng = np.random.default_rng(7)
-    rows = np.arange(w.T) if w.T <= 256 else \
-        np.unique(np.r_[0, 1, w.T - 1, rng.integers(0, w.T, 768)])
-    ref = oracle_gate(o, gi, cfg, rows)
+    # the oracle on every token (its float64 logits once, then its selection)
+    rows = np.arange(w.T)
+    lg64 = o.logits(gi.x, gi.W)
+    ref = o.select(lg64, gi.bias, cfg.n_group, cfg.topk_group, cfg.top_k,
+                   cfg.route_scale, cfg.order, with_scores=True)
     stats = compare_gate(w_np, i_np, ref, w.cfg.route_scale, rows, topk_group=w.cfg.topk_group)
     lg_all = sg.siggate_logits(x, W, cfg).cpu().numpy()
     lg = lg_all[rows]
-    stats.update(score_error(lg, o.logits(gi.x[rows], gi.W), gi.bias, ref.margins,
+    stats.update(score_error(lg, lg64, gi.bias, ref.margins,
                              np.all(i_np[rows] == ref.indices, axis=1)))
     # every token: the oracle's selection on the GPU's own logits (the
     # selection epilogue apart from the GEMM's rounding), same rules
