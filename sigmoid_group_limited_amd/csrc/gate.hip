@@ -83,6 +83,63 @@ __device__ __forceinline__ float readlane_f(float v, int lane)
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
 }
 
+// Lane exchanges through DPP (register crossbar of the VALU; no LDS round
+// trip as with a shuffle).  Each pairs lane i with a partner inside its
+// group of 4, 8 or 16 lanes, the groups split into disjoint halves, so
+// repeated merges over xor1, xor2, the half-row mirror and the row mirror
+// combine 2, 4, 8 and 16 lanes.
+enum DppCtrl {
+    DPP_XOR1 = 0xB1,          // quad_perm [1,0,3,2]
+    DPP_XOR2 = 0x4E,          // quad_perm [2,3,0,1]
+    DPP_HALF_MIRROR = 0x141,  // i <-> 7-i inside 8 lanes
+    DPP_MIRROR = 0x140,       // i <-> 15-i inside 16 lanes
+    DPP_BCAST15 = 0x142,      // lane 15 of a row to the whole next row
+    DPP_BCAST31 = 0x143,      // lane 31 to rows 2 and 3
+};
+template <int CTRL>
+__device__ __forceinline__ unsigned dpp_u(unsigned x)
+{
+    return (unsigned)__builtin_amdgcn_update_dpp((int)x, (int)x, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(x), __float_as_int(x), CTRL,
+                                                      0xF, 0xF, false));
+}
+
+// Largest and smallest x over the wave's 64 lanes (every lane gets both):
+// merges inside rows of 16 lanes, then rows 0+1 into row 1 and 2+3 into
+// row 3 (row_bcast:15; rows 0 and 2 keep their value), then rows 0..3 into
+// row 3 (row_bcast:31), whose lane 63 holds the result.
+__device__ __forceinline__ void wave_max_min(uint32_t &hi, uint32_t &lo)
+{
+    hi = max(hi, dpp_u<DPP_XOR1>(hi));
+    lo = min(lo, dpp_u<DPP_XOR1>(lo));
+    hi = max(hi, dpp_u<DPP_XOR2>(hi));
+    lo = min(lo, dpp_u<DPP_XOR2>(lo));
+    hi = max(hi, dpp_u<DPP_HALF_MIRROR>(hi));
+    lo = min(lo, dpp_u<DPP_HALF_MIRROR>(lo));
+    hi = max(hi, dpp_u<DPP_MIRROR>(hi));
+    lo = min(lo, dpp_u<DPP_MIRROR>(lo));
+    hi = max(hi, (unsigned)__builtin_amdgcn_update_dpp((int)hi, (int)hi, DPP_BCAST15, 0xA, 0xF, false));
+    lo = min(lo, (unsigned)__builtin_amdgcn_update_dpp((int)lo, (int)lo, DPP_BCAST15, 0xA, 0xF, false));
+    hi = max(hi, (unsigned)__builtin_amdgcn_update_dpp((int)hi, (int)hi, DPP_BCAST31, 0xC, 0xF, false));
+    lo = min(lo, (unsigned)__builtin_amdgcn_update_dpp((int)lo, (int)lo, DPP_BCAST31, 0xC, 0xF, false));
+    hi = (uint32_t)__builtin_amdgcn_readlane((int)hi, 63);
+    lo = (uint32_t)__builtin_amdgcn_readlane((int)lo, 63);
+}
+
+// The two largest values of a lane set (m1 >= m2, multiplicity counted)
+// merged with the partner lane's pair.
+__device__ __forceinline__ void merge_top2(float &m1, float &m2, float o1, float o2)
+{
+    const float hi = fmaxf(m1, o1);
+    const float lo = fminf(m1, o1);
+    m2 = fmaxf(lo, fmaxf(m2, o2));
+    m1 = hi;
+}
+
 // Selection for one token held by one wave.  Lane l owns experts
 // [l*V, l*V + V) and their logits lg[].  `scratch` is wave-private LDS of at
 // least 3 * MAX_TOPK words.  Writes row t of weights and indices.
@@ -141,14 +198,13 @@ __device__ __forceinline__ void select_token(const float (&lg)[V], const float (
                 m2 = x;
             }
         }
-        for (int off = 1; off < lpg; off <<= 1) {
-            const float o1 = __shfl_xor(m1, off);
-            const float o2 = __shfl_xor(m2, off);
-            const float hi = fmaxf(m1, o1);
-            const float lo = fminf(m1, o1);
-            m2 = fmaxf(lo, fmaxf(m2, o2));
-            m1 = hi;
-        }
+        // merge over the group's lanes: DPP inside 16 lanes, shuffles
+        // across rows (groups of 32 or 64 lanes)
+        if (lpg >= 2) merge_top2(m1, m2, dpp_f<DPP_XOR1>(m1), dpp_f<DPP_XOR1>(m2));
+        if (lpg >= 4) merge_top2(m1, m2, dpp_f<DPP_XOR2>(m1), dpp_f<DPP_XOR2>(m2));
+        if (lpg >= 8) merge_top2(m1, m2, dpp_f<DPP_HALF_MIRROR>(m1), dpp_f<DPP_HALF_MIRROR>(m2));
+        if (lpg >= 16) merge_top2(m1, m2, dpp_f<DPP_MIRROR>(m1), dpp_f<DPP_MIRROR>(m2));
+        for (int off = 16; off < lpg; off <<= 1) merge_top2(m1, m2, __shfl_xor(m1, off), __shfl_xor(m2, off));
         // with a bias: top-2 sum; without: the group maximum
         const float gs = a.bias ? m1 + m2 : m1;
         const int g = lane / lpg;
@@ -173,30 +229,54 @@ __device__ __forceinline__ void select_token(const float (&lg)[V], const float (
     // Bracket the K-th largest key X: X <= the wave maximum hi, and, when at
     // least K lanes hold a key above -inf, X >= the K-th largest of those
     // lanes' maxima >= the smallest of them, lo.  X then shares every bit
-    // above the first one where hi and lo differ, so the search below
-    // starts there with those bits set.
+    // above the first one where its bounds differ, so a search starts there
+    // with those bits set.
     uint32_t lm = key[0];
 #pragma unroll
     for (int j = 1; j < V; ++j) lm = max(lm, key[j]);
     const uint32_t none = orderable(-INFINITY);
     uint32_t hi = lm, lo = lm > none ? lm : 0xffffffffu;
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        hi = max(hi, (uint32_t)__shfl_xor((int)hi, off));
-        lo = min(lo, (uint32_t)__shfl_xor((int)lo, off));
-    }
+    wave_max_min(hi, lo);
     uint32_t kth = 0;
     int b_top = 31;
     if (__popcll(__ballot(lm > none)) >= K) {
-        const uint32_t diff = hi ^ lo;
-        b_top = diff ? 31 - __clz(diff) : -1;
-        kth = b_top < 0 ? hi : hi & ~(0xffffffffu >> (31 - b_top));
+        // A tighter lower bound first: a key lk that at least K lane
+        // maxima reach (the K-th largest lane maximum, or a prefix of it
+        // that exactly K reach), by the same bit search over one key per
+        // lane -- one compare per bit instead of V.  At least K keys reach
+        // lk, so lk <= X.  If exactly K keys reach it -- the usual case: no
+        // lane holds two of the winners -- those K are the winners and X
+        // is not needed beyond lk.
+        uint32_t diff = hi ^ lo;
+        int bb = diff ? 31 - __clz(diff) : -1;
+        uint32_t lk = bb < 0 ? hi : hi & ~(0xffffffffu >> (31 - bb));
+        for (; bb >= 0; --bb) {
+            const uint32_t cand = lk | (1u << bb);
+            const int c = __popcll(__ballot(lm >= cand));
+            if (c >= K) {
+                lk = cand;
+                if (c == K) break;
+            }
+        }
+        int c0 = 0;
+#pragma unroll
+        for (int j = 0; j < V; ++j) c0 += __popcll(__ballot(key[j] >= lk));
+        if (c0 == K) {
+            kth = lk;
+            b_top = -1;
+        } else {
+            diff = hi ^ lk;
+            b_top = diff ? 31 - __clz(diff) : -1;
+            kth = b_top < 0 ? hi : hi & ~(0xffffffffu >> (31 - b_top));
+        }
     }
 
     // K-th largest key, most significant bit first.  Once exactly K keys
     // are >= the prefix found so far, those K are the winners and the lower
     // bits cannot change the choice: stop there (the counts are ballots, so
-    // every lane takes the same branch).
+    // every lane takes the same branch).  (Two bits per step -- three
+    // candidates counted at once -- measured slower: the loop is bound by
+    // the issue of its compares and counts, not by their latency.)
     for (int b = b_top; b >= 0; --b) {
         const uint32_t cand = kth | (1u << b);
         int cnt = 0;
@@ -687,19 +767,19 @@ __device__ __forceinline__ void load_row(const float *p, float (&v)[V])
     }
 }
 
-// A token's summed logits: written out, or through the selection.
+// A token's summed logits: written out, or through the selection (bias_r:
+// this lane's bias values, loaded at kernel entry so that their latency
+// overlaps the partial loads instead of following the sum).
 template <int V, int MODE>
 __device__ __forceinline__ void finish_reduce(const GateArgs &a, const float (&lg)[V],
-                                              const int lane, const int t, float *scratch)
+                                              const float (&bias_r)[V], const int lane, const int t,
+                                              float *scratch)
 {
     constexpr int E = V * 64;
     if constexpr (MODE == MODE_LOGITS) {
 #pragma unroll
         for (int j = 0; j < V; ++j) a.logits[(size_t)t * E + lane * V + j] = lg[j];
     } else {
-        float bias_r[V];
-#pragma unroll
-        for (int j = 0; j < V; ++j) bias_r[j] = a.bias ? a.bias[lane * V + j] : 0.0f;
         select_token<V>(lg, bias_r, lane, a, t, scratch);
     }
 }
@@ -725,13 +805,16 @@ __global__ __launch_bounds__(64 * NWR) void gate_reduce_kernel(GateArgs a)
     const int s1 = min(s0 + per, a.n_split);
     const float *const p = a.partial + (size_t)t * E + lane * V;
     const size_t slice = (size_t)a.T * E;
+    float bias_r[V];
+#pragma unroll
+    for (int j = 0; j < V; ++j) bias_r[j] = MODE == MODE_SELECT && a.bias ? a.bias[lane * V + j] : 0.0f;
     float lg[V];
 #pragma unroll
     for (int j = 0; j < V; ++j) lg[j] = 0.0f;
     if constexpr (NWR == 1) {
         if (a.n_split == 1) {   // a single slice: the logits themselves
             load_row<V>(p, lg);
-            finish_reduce<V, MODE>(a, lg, lane, t, scratch);
+            finish_reduce<V, MODE>(a, lg, bias_r, lane, t, scratch);
             return;
         }
         // one wave, at most ONE_WAVE_SLICES slices: every load is issued
@@ -747,7 +830,7 @@ __global__ __launch_bounds__(64 * NWR) void gate_reduce_kernel(GateArgs a)
 #pragma unroll
                 for (int j = 0; j < V; ++j) lg[j] += q[u][j];
             }
-        finish_reduce<V, MODE>(a, lg, lane, t, scratch);
+        finish_reduce<V, MODE>(a, lg, bias_r, lane, t, scratch);
         return;
     }
     int s = s0;
@@ -774,7 +857,7 @@ __global__ __launch_bounds__(64 * NWR) void gate_reduce_kernel(GateArgs a)
     for (int w = 1; w < NWR; ++w)
 #pragma unroll
         for (int j = 0; j < V; ++j) lg[j] += part[w][lane * V + j];
-    finish_reduce<V, MODE>(a, lg, lane, t, scratch);
+    finish_reduce<V, MODE>(a, lg, bias_r, lane, t, scratch);
 }
 
 // Largest E with 64-token fused tiles: their double-buffered stage of W and x,
