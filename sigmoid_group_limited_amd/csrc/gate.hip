@@ -784,7 +784,7 @@ __device__ __forceinline__ void finish_reduce(const GateArgs &a, const float (&l
     }
 }
 
-constexpr int ONE_WAVE_SLICES = 16;
+constexpr int ONE_WAVE_SLICES = 24;
 
 // Adds the n_split partial logits of one token in a fixed order -- wave w
 // of NWR sums its contiguous run of slices in ascending order, then wave 0
@@ -818,12 +818,17 @@ __global__ __launch_bounds__(64 * NWR) void gate_reduce_kernel(GateArgs a)
             return;
         }
         // one wave, at most ONE_WAVE_SLICES slices: every load is issued
-        // before the first add (slices past n_split re-read the last one and
-        // are not added)
+        // before the first add
         float q[ONE_WAVE_SLICES][V];
 #pragma unroll
-        for (int u = 0; u < ONE_WAVE_SLICES; ++u)
-            load_row<V>(p + (size_t)min(u, a.n_split - 1) * slice, q[u]);
+        for (int u = 0; u < ONE_WAVE_SLICES; ++u) {
+            if (u < a.n_split) {
+                load_row<V>(p + (size_t)u * slice, q[u]);
+            } else {
+#pragma unroll
+                for (int j = 0; j < V; ++j) q[u][j] = 0.0f;
+            }
+        }
 #pragma unroll
         for (int u = 0; u < ONE_WAVE_SLICES; ++u)
             if (u < a.n_split) {

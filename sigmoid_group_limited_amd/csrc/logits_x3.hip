@@ -307,17 +307,38 @@ __global__ __launch_bounds__(512) void x3_gemm8_kernel(GateArgs a)
             store_x(0, 0, xr[0]);
             load_x(min(PW, npairs - 1), xr[0]);
             __syncthreads();
+            // One W fragment per wave (NBW = 1): chunk j's MFMAs run on W
+            // split one step earlier, and the split of chunk j+1 (ring slot
+            // u1, then refilled with chunk j+1+PW) is issued beside them, so
+            // its VALU work overlaps the matrix work.  Wider tiles keep the
+            // split in front of the MFMAs (two splits in flight would not fit
+            // their registers).
+            constexpr bool AHEAD = NBW == 1;
+            u32x4 bw[NBW][3];
+            if constexpr (AHEAD) {
+#pragma unroll
+                for (int n = 0; n < NBW; ++n) {
+                    split3(wr[0][n][0], wr[0][n][1], bw[n][0], bw[n][1], bw[n][2]);
+                    wfrag32(min(PW, npairs - 1), n, wr[0][n]);
+                }
+            }
             auto step = [&](int j, int u) {   // u = j % PW; PW is even, so j%2 = u%2
                 const int sb = u & 1;
+                const int u1 = (u + 1) % PW;
                 const u32x4 *const xs = smem + sb * BM * 8;
                 u32x4 af[MB];
 #pragma unroll
                 for (int m = 0; m < MB; ++m) af[m] = xs[xw_slot(16 * m + f_row, 4 * wk + (lane >> 4))];
-                u32x4 bw[NBW][3];
+                u32x4 bn[NBW][3];
 #pragma unroll
                 for (int n = 0; n < NBW; ++n) {
-                    split3(wr[u][n][0], wr[u][n][1], bw[n][0], bw[n][1], bw[n][2]);
-                    wfrag32(min(j + PW, npairs - 1), n, wr[u][n]);
+                    if constexpr (AHEAD) {
+                        split3(wr[u1][n][0], wr[u1][n][1], bn[n][0], bn[n][1], bn[n][2]);
+                        wfrag32(min(j + 1 + PW, npairs - 1), n, wr[u1][n]);
+                    } else {
+                        split3(wr[u][n][0], wr[u][n][1], bw[n][0], bw[n][1], bw[n][2]);
+                        wfrag32(min(j + PW, npairs - 1), n, wr[u][n]);
+                    }
                 }
 #pragma unroll
                 for (int pl = 0; pl < 3; ++pl)
@@ -326,7 +347,12 @@ __global__ __launch_bounds__(512) void x3_gemm8_kernel(GateArgs a)
 #pragma unroll
                         for (int m = 0; m < MB; ++m) acc[m][n] = mfma_bf16(af[m], bw[n][pl], acc[m][n]);
                 __builtin_amdgcn_sched_barrier(0);
-                const int u1 = (u + 1) % PW;
+                if constexpr (AHEAD) {
+#pragma unroll
+                    for (int n = 0; n < NBW; ++n)
+#pragma unroll
+                        for (int pl = 0; pl < 3; ++pl) bw[n][pl] = bn[n][pl];
+                }
                 store_x(min(j + 1, npairs - 1), sb ^ 1, xr[u1]);
                 load_x(min(j + 1 + PW, npairs - 1), xr[u1]);
                 __syncthreads();
@@ -420,7 +446,7 @@ __global__ __launch_bounds__(512) void x3_gemm8_kernel(GateArgs a)
 struct X3Shape {
     int bm, nbw;
 };
-constexpr X3Shape X3_SHAPES[] = {{128, 3}, {128, 2}, {64, 2}, {64, 1}};
+constexpr X3Shape X3_SHAPES[] = {{128, 3}, {128, 2}, {128, 1}, {64, 2}, {64, 1}};
 
 // Cost model, in MFMA cycles of one SIMD: a chunk of a BM x 64*NBW tile is
 // 3 * (BM/16) * NBW MFMAs of 16 cycles plus X3_CHUNK_OVERHEAD; a workgroup
@@ -508,6 +534,7 @@ hipError_t launch_x3_gemm(const GateArgs &args, const GatePlan &p, hipStream_t s
     if (p.x3_bm == 128 && p.x3_nbw == 3) return launch_shape<128, 3>(a, p, stream);
     if (p.x3_bm == 128 && p.x3_nbw == 2) return launch_shape<128, 2>(a, p, stream);
     if (p.x3_bm == 64 && p.x3_nbw == 2) return launch_shape<64, 2>(a, p, stream);
+    if (p.x3_bm == 128 && p.x3_nbw == 1) return launch_shape<128, 1>(a, p, stream);
     if (p.x3_bm == 64 && p.x3_nbw == 1) return launch_shape<64, 1>(a, p, stream);
     return hipErrorInvalidValue;
 }
