@@ -442,19 +442,30 @@ __global__ __launch_bounds__(512) void x3_gemm8_kernel(GateArgs a)
         }
 }
 
-// Tile shapes: BM tokens x 64*NBW experts.
+// Tile shapes: BM tokens x 64*NBW experts.  Large batches (W pre-split
+// into planes) choose among all; small batches, which split W in registers,
+// among the one-fragment tiles only (a sweep over shapes and slice counts at
+// T = 1 ... 1000 found one of them fastest at every T).
 struct X3Shape {
     int bm, nbw;
 };
-constexpr X3Shape X3_SHAPES[] = {{128, 3}, {128, 2}, {128, 1}, {64, 2}, {64, 1}};
+constexpr X3Shape X3_SHAPES_PRESPLIT[] = {{128, 3}, {128, 2}, {64, 2}, {64, 1}};
+constexpr X3Shape X3_SHAPES_SPLIT[] = {{128, 1}, {64, 1}};
 
-// Cost model, in MFMA cycles of one SIMD: a chunk of a BM x 64*NBW tile is
-// 3 * (BM/16) * NBW MFMAs of 16 cycles plus X3_CHUNK_OVERHEAD; a workgroup
-// adds X3_LATENCY; workgroups beyond one per compute unit queue behind it;
-// the partial logits cross HBM twice at X3_BYTES_PER_CYCLE.
+// Cost model, in cycles of one SIMD per 32-column unit of a workgroup's
+// k-slice: large batches, 3 * (BM/16) * NBW MFMAs of 16 cycles plus
+// X3_CHUNK_OVERHEAD; small batches, X3_SPLIT_CHUNK_FIXED plus
+// X3_SPLIT_CHUNK_PER_BLOCK per 16-token block (fitted to graph-replayed gate
+// times over tile shapes and slice counts at T = 1 ... 1000, E = 128 ... 512:
+// the in-register split and the memory pipeline, not the MFMAs, set the pace
+// there).  A workgroup adds X3_LATENCY; workgroups beyond one per compute
+// unit queue behind it; the partial logits cross memory twice at
+// X3_BYTES_PER_CYCLE.
 constexpr double X3_CHUNK_OVERHEAD = 150.0;
 constexpr double X3_LATENCY = 3000.0;
 constexpr double X3_BYTES_PER_CYCLE = 2400.0;
+constexpr double X3_SPLIT_CHUNK_FIXED = 300.0;
+constexpr double X3_SPLIT_CHUNK_PER_BLOCK = 20.0;
 constexpr int X3_N_CU = 256;
 // From this many tokens on, W is split once per call into planes (the split
 // kernel reads W once and writes 1.5x its bytes) instead of in registers by
@@ -482,13 +493,16 @@ GatePlan plan_x3(int T, int d, int E)
     const int chunks = (d + KC - 1) / KC;
     double best = 1e300;
     const bool presplit = T >= X3_PRESPLIT_MIN_T;
-    for (const X3Shape &sh : X3_SHAPES) {
+    const X3Shape *const shapes = presplit ? X3_SHAPES_PRESPLIT : X3_SHAPES_SPLIT;
+    const int n_shapes = presplit ? (int)(sizeof(X3_SHAPES_PRESPLIT) / sizeof(X3Shape))
+                                  : (int)(sizeof(X3_SHAPES_SPLIT) / sizeof(X3Shape));
+    for (int i = 0; i < n_shapes; ++i) {
+        const X3Shape &sh = shapes[i];
         const int bn = 64 * sh.nbw;
         if (E % bn != 0) continue;
-        // the in-register split of a 128 x 192 tile does not fit 256 VGPRs
-        if (!presplit && sh.bm == 128 && sh.nbw == 3) continue;
         const long tiles = ((long)T + sh.bm - 1) / sh.bm * (E / bn);
-        const double chunk_cost = 3.0 * (sh.bm / 16) * sh.nbw * 16.0 + X3_CHUNK_OVERHEAD;
+        const double chunk_cost = presplit ? 3.0 * (sh.bm / 16) * sh.nbw * 16.0 + X3_CHUNK_OVERHEAD
+                                           : X3_SPLIT_CHUNK_FIXED + X3_SPLIT_CHUNK_PER_BLOCK * (sh.bm / 16) * sh.nbw;
         for (int s = 1; s <= chunks; ++s) {
             const int cps = (chunks + s - 1) / s;
             if ((chunks + cps - 1) / cps != s) continue;   // s slices of cps chunks
