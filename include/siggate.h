@@ -41,7 +41,7 @@
  *   - NaN or Inf in x, W or bias give undefined selections.
  *
  * Supported shapes (others return SIGGATE_EUNSUPPORTED):
- *   E in {128, 256, 384, 512}; n_group a power of two with 1 <= n_group <= 64;
+ *   E a multiple of 64 up to 512; n_group a power of two with 1 <= n_group <= 64;
  *   1 <= top_k <= 8; d a positive multiple of 8; 0 <= T <= 2^31 / top_k.
  * Invalid configurations return SIGGATE_EINVAL: topk_group outside
  * [1, n_group], top_k > topk_group * E / n_group, order not 0 or 1,

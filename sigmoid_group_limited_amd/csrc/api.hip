@@ -38,7 +38,7 @@ siggate_status_t check_gate_cfg(const siggate_cfg_t *c)
     if (c->mask_zero != 0 && c->mask_zero != 1) return SIGGATE_EINVAL;
     if (!(c->denom_eps >= 0.0f)) return SIGGATE_EINVAL;               // negative or NaN
     if (c->logits_path != PATH_FP32 && c->logits_path != PATH_BF16X3) return SIGGATE_EINVAL;
-    if (c->E != 128 && c->E != 256 && c->E != 384 && c->E != 512) return SIGGATE_EUNSUPPORTED;
+    if (c->E % 64 != 0 || c->E > MAX_EXPERTS) return SIGGATE_EUNSUPPORTED;
     if (c->n_group > 64 || (c->n_group & (c->n_group - 1)) != 0) return SIGGATE_EUNSUPPORTED;
     if (c->top_k > MAX_TOPK) return SIGGATE_EUNSUPPORTED;
     if (c->d % 8 != 0) return SIGGATE_EUNSUPPORTED;
@@ -115,6 +115,7 @@ GateArgs gate_args(const void *x, const float *W, const float *bias, const sigga
     a.mask_zero = c->mask_zero;
     a.denom_eps = c->denom_eps;
     a.E = c->E;
+    a.e_stride = p.e_stride;
     a.chunks_total = (c->d + KC - 1) / KC;
     a.chunks_per_split = p.chunks_per_split;
     a.n_split = p.n_split;

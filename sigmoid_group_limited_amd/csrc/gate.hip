@@ -349,8 +349,10 @@ __device__ __forceinline__ void select_token(const float (&lg)[V], const float (
 }
 
 // Writes a finished BM x E logits tile: as partial or final logits, or
-// through LDS (never HBM) into the selection, BM/NW tokens per wave.
-template <int E, int MB, int NW, int MODE>
+// through LDS (never HBM) into the selection, BM/NW tokens per wave.  ER is
+// the number of real experts: the tile's columns past ER are padding (E
+// rounded up to whole 128-expert tiles) and are neither written nor ranked.
+template <int E, int MB, int NW, int MODE, int ER>
 __device__ __forceinline__ void finish_tile(const GateArgs &a,
                                             f32x16 (&acc)[Shape<E, MB, NW>::MBW][Shape<E, MB, NW>::NB],
                                             float *smem, const int t0, const int e0, const int ks,
@@ -366,7 +368,9 @@ __device__ __forceinline__ void finish_tile(const GateArgs &a,
     const int r_base = wm * S::MBW * 32 + 4 * (lane >> 5);
 
     if constexpr (MODE == MODE_PARTIAL || MODE == MODE_LOGITS) {
-        float *out = MODE == MODE_PARTIAL ? a.partial + (size_t)ks * a.T * a.E : a.logits;
+        // partial rows are e_stride long (whole tiles); final logits rows E
+        const int stride = MODE == MODE_PARTIAL ? a.e_stride : a.E;
+        float *out = MODE == MODE_PARTIAL ? a.partial + (size_t)ks * a.T * a.e_stride : a.logits;
 #pragma unroll
         for (int m = 0; m < S::MBW; ++m)
 #pragma unroll
@@ -374,7 +378,8 @@ __device__ __forceinline__ void finish_tile(const GateArgs &a,
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int t = t0 + m * 32 + 8 * (r >> 2) + r_base + (r & 3);
-                    if (has_acc && t < a.T) out[(size_t)t * a.E + e_base + n * 32] = acc[m][n][r];
+                    const bool real = MODE == MODE_PARTIAL || ER == E || e_base + n * 32 < ER;
+                    if (has_acc && t < a.T && real) out[(size_t)t * stride + e_base + n * 32] = acc[m][n][r];
                 }
     } else {
         // Scores go to LDS (never to HBM); each wave then selects for BM/NW
@@ -393,7 +398,7 @@ __device__ __forceinline__ void finish_tile(const GateArgs &a,
         }
         __syncthreads();
 
-        constexpr int V = S::V;
+        constexpr int V = ER / 64;
         float bias_r[V];
 #pragma unroll
         for (int j = 0; j < V; ++j) bias_r[j] = a.bias ? a.bias[lane * V + j] : 0.0f;
@@ -417,7 +422,7 @@ __device__ __forceinline__ void finish_tile(const GateArgs &a,
 // 2 * FLUSH_CHUNKS chunks, whose chains the slicing already keeps short --
 // the branch in the unrolled loop measurably slows those short tiles, and
 // long split tiles run it with P = 2, where it costs least).
-template <int E, int MB, int NW, int MODE, int P, bool BLOCKED>
+template <int E, int MB, int NW, int MODE, int P, bool BLOCKED, int ER = E>
 __global__ __launch_bounds__(64 * NW) void gate_gemm_kernel(GateArgs a)
 {
     using S = Shape<E, MB, NW>;
@@ -474,13 +479,22 @@ __global__ __launch_bounds__(64 * NW) void gate_gemm_kernel(GateArgs a)
     const float *const Wp = a.W + (size_t)(e0 + w_row) * d;
     const uint16_t *const Xp = a.x + (size_t)x_t * d;
 
+    // Expert rows past E -- when E is an odd multiple of 64, the last 64
+    // rows of the last tile, which pad it to 128 -- are never read: that row
+    // block reads the tile's first rows instead and is stored as zeros, so
+    // the padding logits are 0 (and are dropped).
+    constexpr bool MAYPAD = MODE == MODE_PARTIAL || ER != E;
+    const bool pad_last = MAYPAD && e0 + (NT / 8) * (WLOADS - 1) >= a.E;
+    const size_t last_off = pad_last ? 0 : (size_t)(WLOADS - 1) * (NT / 8) * d;
     auto load_global = [&](int c, Stage &st) {
         const int k0 = c * KC;
         const int wc = min(k0 + w_col, d - 4);
         const int xc = min(k0 + x_col, d - XE);
 #pragma unroll
-        for (int i = 0; i < WLOADS; ++i)
-            st.w[i] = *(const f32x4 *)(Wp + (size_t)i * (NT / 8) * d + wc);
+        for (int i = 0; i < WLOADS; ++i) {
+            const size_t off = MAYPAD && i == WLOADS - 1 ? last_off : (size_t)i * (NT / 8) * d;
+            st.w[i] = *(const f32x4 *)(Wp + off + wc);
+        }
         st.x = *(const xvec *)(Xp + xc);
     };
     auto store_lds = [&](int c, int buf, const Stage &st) {
@@ -488,8 +502,11 @@ __global__ __launch_bounds__(64 * NW) void gate_gemm_kernel(GateArgs a)
         const bool xk = k0 + x_col < d;
         float *wb = Ws + buf * E * KPAD;
 #pragma unroll
-        for (int i = 0; i < WLOADS; ++i)
-            *(f32x4 *)(wb + (w_row + (NT / 8) * i) * KPAD + w_col) = st.w[i];
+        for (int i = 0; i < WLOADS; ++i) {
+            const bool zero = MAYPAD && i == WLOADS - 1 && pad_last;
+            *(f32x4 *)(wb + (w_row + (NT / 8) * i) * KPAD + w_col) =
+                zero ? f32x4{0.0f, 0.0f, 0.0f, 0.0f} : st.w[i];
+        }
         float *xb = Xs + buf * S::BM * KPAD + x_row * KPAD + x_col;
         if constexpr (XE >= 4) {
 #pragma unroll
@@ -740,11 +757,11 @@ __global__ __launch_bounds__(64 * NW) void gate_gemm_kernel(GateArgs a)
         __syncthreads();
     }
 
-    finish_tile<E, MB, NW, MODE>(a, acc, smem, t0, e0, ks, wave, lane, wm, wk == 0);
+    finish_tile<E, MB, NW, MODE, ER>(a, acc, smem, t0, e0, ks, wave, lane, wm, wk == 0);
 }
 
-// V consecutive floats from p (V even; p 8-byte aligned, 16-byte when V is
-// a multiple of 4).
+// V consecutive floats from p (p 8-byte aligned when V is even, 16-byte
+// when V is a multiple of 4; single loads for odd V).
 template <int V>
 __device__ __forceinline__ void load_row(const float *p, float (&v)[V])
 {
@@ -755,8 +772,7 @@ __device__ __forceinline__ void load_row(const float *p, float (&v)[V])
 #pragma unroll
             for (int i = 0; i < 4; ++i) v[4 * h + i] = q[i];
         }
-    } else {
-        static_assert(V % 2 == 0, "rows are loaded in float pairs");
+    } else if constexpr (V % 2 == 0) {
         typedef float f32x2 __attribute__((ext_vector_type(2)));
 #pragma unroll
         for (int h = 0; h < V / 2; ++h) {
@@ -764,6 +780,9 @@ __device__ __forceinline__ void load_row(const float *p, float (&v)[V])
             v[2 * h] = q[0];
             v[2 * h + 1] = q[1];
         }
+    } else {
+#pragma unroll
+        for (int h = 0; h < V; ++h) v[h] = p[h];
     }
 }
 
@@ -803,8 +822,9 @@ __global__ __launch_bounds__(64 * NWR) void gate_reduce_kernel(GateArgs a)
     const int per = (a.n_split + NWR - 1) / NWR;
     const int s0 = min(wave * per, a.n_split);
     const int s1 = min(s0 + per, a.n_split);
-    const float *const p = a.partial + (size_t)t * E + lane * V;
-    const size_t slice = (size_t)a.T * E;
+    // partial rows are e_stride floats long (E rounded up to whole tiles)
+    const float *const p = a.partial + (size_t)t * a.e_stride + lane * V;
+    const size_t slice = (size_t)a.T * a.e_stride;
     float bias_r[V];
 #pragma unroll
     for (int j = 0; j < V; ++j) bias_r[j] = MODE == MODE_SELECT && a.bias ? a.bias[lane * V + j] : 0.0f;
@@ -870,7 +890,9 @@ __global__ __launch_bounds__(64 * NWR) void gate_reduce_kernel(GateArgs a)
 // where the fused path uses 32-token tiles only.
 constexpr int MAX_E_TILE64 = 384;
 
-template <int E>
+// E: the GEMM's expert tile width (whole 128-expert tiles); ER: the real
+// expert count (E, or E - 64 when that is an odd multiple of 64).
+template <int E, int ER>
 hipError_t launch_for_e(const GateArgs &a, const GatePlan &p, GateMode final_mode,
                         hipStream_t stream)
 {
@@ -881,13 +903,13 @@ hipError_t launch_for_e(const GateArgs &a, const GatePlan &p, GateMode final_mod
         const dim3 grid(p.grid), block(64 * 8);
         if constexpr (E <= MAX_E_TILE64) {
             if (p.m_blocks == 2)
-                return sel ? launch_kernel(gate_gemm_kernel<E, 2, 8, MODE_SELECT, 2, true>, grid, block, stream, a)
-                           : launch_kernel(gate_gemm_kernel<E, 2, 8, MODE_LOGITS, 2, true>, grid, block, stream, a);
+                return sel ? launch_kernel(gate_gemm_kernel<E, 2, 8, MODE_SELECT, 2, true, ER>, grid, block, stream, a)
+                           : launch_kernel(gate_gemm_kernel<E, 2, 8, MODE_LOGITS, 2, true, ER>, grid, block, stream, a);
         }
         // one register stage of loads ahead at E = 512, where two would spill
         constexpr int P1 = E > MAX_E_TILE64 ? 1 : 2;
-        return sel ? launch_kernel(gate_gemm_kernel<E, 1, 8, MODE_SELECT, P1, true>, grid, block, stream, a)
-                   : launch_kernel(gate_gemm_kernel<E, 1, 8, MODE_LOGITS, P1, true>, grid, block, stream, a);
+        return sel ? launch_kernel(gate_gemm_kernel<E, 1, 8, MODE_SELECT, P1, true, ER>, grid, block, stream, a)
+                   : launch_kernel(gate_gemm_kernel<E, 1, 8, MODE_LOGITS, P1, true, ER>, grid, block, stream, a);
     }
     // split GEMM: 32 tokens x 128 experts, 8 waves (two per SIMD): 4 columns
     // of 32 experts x 2 k-halves of every chunk; or the bfloat16 three-way
@@ -908,11 +930,11 @@ hipError_t launch_for_e(const GateArgs &a, const GatePlan &p, GateMode final_mod
     // contiguous run of them
     const dim3 rgrid(a.T);
     if (p.n_split <= ONE_WAVE_SLICES)
-        return sel ? launch_kernel(gate_reduce_kernel<E, MODE_SELECT, 1>, rgrid, dim3(64), stream, a)
-                   : launch_kernel(gate_reduce_kernel<E, MODE_LOGITS, 1>, rgrid, dim3(64), stream, a);
-    constexpr int NWR = E > MAX_E_TILE64 ? 8 : 16;
-    return sel ? launch_kernel(gate_reduce_kernel<E, MODE_SELECT, NWR>, rgrid, dim3(64 * NWR), stream, a)
-               : launch_kernel(gate_reduce_kernel<E, MODE_LOGITS, NWR>, rgrid, dim3(64 * NWR), stream, a);
+        return sel ? launch_kernel(gate_reduce_kernel<ER, MODE_SELECT, 1>, rgrid, dim3(64), stream, a)
+                   : launch_kernel(gate_reduce_kernel<ER, MODE_LOGITS, 1>, rgrid, dim3(64), stream, a);
+    constexpr int NWR = ER > MAX_E_TILE64 ? 8 : 16;
+    return sel ? launch_kernel(gate_reduce_kernel<ER, MODE_SELECT, NWR>, rgrid, dim3(64 * NWR), stream, a)
+               : launch_kernel(gate_reduce_kernel<ER, MODE_LOGITS, NWR>, rgrid, dim3(64 * NWR), stream, a);
 }
 
 }  // namespace
@@ -934,6 +956,9 @@ GatePlan plan_gate(int T, int d, int E, int path)
 {
     if (path == PATH_BF16X3) return plan_x3(T, d, E);
     GatePlan p{};
+    // the GEMM's expert tiles are whole 128-expert tiles
+    const int EP = (E + 127) / 128 * 128;
+    p.e_stride = EP;
     const int chunks = (d + KC - 1) / KC;
     const long tiles64 = ((long)T + 63) / 64;
     const long tiles32 = ((long)T + 31) / 32;
@@ -947,7 +972,7 @@ GatePlan plan_gate(int T, int d, int E, int path)
     // ones, and a partly filled last round costs a whole one.
     if (tiles64 >= N_CU || tiles32 >= N_CU) {
         const long r64 = (tiles64 + N_CU - 1) / N_CU, r32 = (tiles32 + N_CU - 1) / N_CU;
-        p.m_blocks = E <= MAX_E_TILE64 && (double)r64 * FUSED_ROUND_RATIO < (double)r32 ? 2 : 1;
+        p.m_blocks = EP <= MAX_E_TILE64 && (double)r64 * FUSED_ROUND_RATIO < (double)r32 ? 2 : 1;
         p.t_tiles = (int)(p.m_blocks == 2 ? tiles64 : tiles32);
         p.grid = p.t_tiles;
         return p;
@@ -955,7 +980,7 @@ GatePlan plan_gate(int T, int d, int E, int path)
     p.split = true;
     p.m_blocks = 1;
     p.t_tiles = (int)tiles32;
-    p.e_tiles = E / 128;
+    p.e_tiles = EP / 128;
     const long tiles = tiles32 * p.e_tiles;
     double best = 1e300;
     for (int s = 1; s <= chunks; ++s) {
@@ -964,7 +989,7 @@ GatePlan plan_gate(int T, int d, int E, int path)
         const long n = tiles * s;
         const double rounds = (double)((n + N_CU - 1) / N_CU);
         const double cost = rounds * (cps + SPLIT_LATENCY) +
-                            2.0 * s * (double)T * E * sizeof(float) / SPLIT_BYTES_PER_UNIT;
+                            2.0 * s * (double)T * EP * sizeof(float) / SPLIT_BYTES_PER_UNIT;
         if (cost < best) {
             best = cost;
             p.n_split = s;
@@ -973,7 +998,7 @@ GatePlan plan_gate(int T, int d, int E, int path)
     }
     const long n = (long)p.t_tiles * p.e_tiles * p.n_split;
     p.grid = (int)((n + 7) / 8 * 8);
-    p.partial_bytes = (size_t)p.n_split * (size_t)T * (size_t)E * sizeof(float);
+    p.partial_bytes = (size_t)p.n_split * (size_t)T * (size_t)EP * sizeof(float);
     return p;
 }
 
@@ -981,10 +1006,14 @@ hipError_t launch_gate(const GateArgs &a, const GatePlan &p, int E, GateMode fin
                        hipStream_t stream)
 {
     switch (E) {
-    case 128: return launch_for_e<128>(a, p, final_mode, stream);
-    case 256: return launch_for_e<256>(a, p, final_mode, stream);
-    case 384: return launch_for_e<384>(a, p, final_mode, stream);
-    case 512: return launch_for_e<512>(a, p, final_mode, stream);
+    case 64: return launch_for_e<128, 64>(a, p, final_mode, stream);
+    case 128: return launch_for_e<128, 128>(a, p, final_mode, stream);
+    case 192: return launch_for_e<256, 192>(a, p, final_mode, stream);
+    case 256: return launch_for_e<256, 256>(a, p, final_mode, stream);
+    case 320: return launch_for_e<384, 320>(a, p, final_mode, stream);
+    case 384: return launch_for_e<384, 384>(a, p, final_mode, stream);
+    case 448: return launch_for_e<512, 448>(a, p, final_mode, stream);
+    case 512: return launch_for_e<512, 512>(a, p, final_mode, stream);
     default: return hipErrorInvalidValue;
     }
 }

@@ -428,7 +428,7 @@ __global__ __launch_bounds__(512) void x3_gemm8_kernel(GateArgs a)
         for (int n = 0; n < NBW; ++n) acc[m][n] = tot[(m * NBW + n) * 64];
     // accumulator r of block (m, n): token t0 + 16m + 4(l/16) + r, expert
     // e0 + 16(NBW*wn + n) + l%16
-    float *const out = a.partial + (size_t)ks * a.T * a.E;
+    float *const out = a.partial + (size_t)ks * a.T * a.e_stride;
 #pragma unroll
     for (int m = 0; m < MB; ++m)
 #pragma unroll
@@ -437,7 +437,7 @@ __global__ __launch_bounds__(512) void x3_gemm8_kernel(GateArgs a)
             if (t < a.T) {
 #pragma unroll
                 for (int n = 0; n < NBW; ++n)
-                    out[(size_t)t * a.E + e0 + 16 * (NBW * wn + n) + f_row] = acc[m][n][r];
+                    out[(size_t)t * a.e_stride + e0 + 16 * (NBW * wn + n) + f_row] = acc[m][n][r];
             }
         }
 }
@@ -490,6 +490,7 @@ GatePlan plan_x3(int T, int d, int E)
 {
     GatePlan p{};
     p.split = true;
+    p.e_stride = E;   // the route's tiles cover E exactly (64-expert multiples)
     const int chunks = (d + KC - 1) / KC;
     double best = 1e300;
     const bool presplit = T >= X3_PRESPLIT_MIN_T;

@@ -40,7 +40,9 @@ struct GateArgs {
     int n_group, topk_group, top_k, order;
     int score_func, renorm, mask_zero;
     float route_scale, denom_eps;
-    int E;                  // experts: row length of logits and partials
+    int E;                  // experts: row length of the logits
+    int e_stride;           // row length of the partials: E, or E rounded up to
+                            // whole 128-expert tiles on the float32 split path
     int chunks_total;       // ceil(d / KC)
     int chunks_per_split;   // KC-chunks of one k-slice
     int n_split;            // k-slices (1 = whole k range in one workgroup)
@@ -72,6 +74,7 @@ struct GatePlan {
     int chunks_per_split;
     int t_tiles, e_tiles;   // split path tiles
     int grid;               // workgroups of the GEMM launch
+    int e_stride;           // row length of the partials (GateArgs::e_stride)
     size_t partial_bytes;   // workspace: split partials (+ x3 planes)
 };
 

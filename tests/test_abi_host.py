@@ -74,6 +74,13 @@ def test_workspace_bytes():
     kimi_big = dataclasses.replace(KIMI.with_T(16384), logits_path=1)
     assert sg.siggate_workspace_bytes(kimi_big) == 16384 * 384 * 4 + 3 * 384 * 7168 * 2
     assert sg.siggate_workspace_bytes(dataclasses.replace(KIMI, logits_path=1)) >= 256 * 384 * 4
+    # E an odd multiple of 64: float32 partial rows span whole 128-expert
+    # tiles, bfloat16x3 ones exactly E
+    e192 = sg.Cfg(256, 7168, 192, 8, 4, 8, 2.5)
+    fp = sg.siggate_workspace_bytes(e192)
+    x3 = sg.siggate_workspace_bytes(dataclasses.replace(e192, logits_path=1))
+    assert fp % (256 * 256 * 4) == 0 and fp >= 256 * 256 * 4
+    assert x3 % (256 * 192 * 4) == 0 and x3 >= 256 * 192 * 4
 
 
 def call_forward(cfg, x=FAKE, W=FAKE, bias=FAKE, w=FAKE, i=FAKE, ws=FAKE, ws_bytes=1 << 40):
@@ -101,7 +108,7 @@ def test_forward_rejects_invalid(bad):
 
 
 @pytest.mark.parametrize("unsup", [
-    dict(E=64, n_group=8), dict(E=640, n_group=8), dict(E=192, n_group=8),
+    dict(E=96, n_group=8), dict(E=640, n_group=8), dict(E=576, n_group=8), dict(E=160, n_group=8),
     dict(n_group=128, topk_group=4, top_k=4), dict(top_k=9, topk_group=8, n_group=8),
     dict(d=7164),
 ])

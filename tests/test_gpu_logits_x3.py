@@ -69,6 +69,12 @@ SMALL = [
     ("e128_g64_kg4_k8_all_kept_T300_d512", wl.GateConfig(128, 64, 4, 8, 1.0), 300, 512),
     ("e512_g8_T200_d7168", wl.GateConfig(512, 8, 4, 8, 2.5), 200, 7168),
     ("e512_g1_T2100_d1000", wl.GateConfig(512, 1, 1, 8, 2.827), 2100, 1000),
+    # odd multiples of 64 experts: 64-expert tiles (and 192-expert ones at 192)
+    ("e192_g8_T100_d7168", wl.GateConfig(192, 8, 4, 8, 2.5), 100, 7168),
+    ("e320_g1_T1500_d1000", wl.GateConfig(320, 1, 1, 8, 2.827), 1500, 1000),
+    ("e448_g8_T64_d4096", wl.GateConfig(448, 8, 4, 8, 1.0), 64, 4096),
+    ("e64_g4_T2000_d512", wl.GateConfig(64, 4, 2, 6, 1.0), 2000, 512),
+    ("e192_g4_T3000_d256", wl.GateConfig(192, 4, 2, 8, 1.0), 3000, 256),
 ]
 
 

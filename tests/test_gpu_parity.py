@@ -85,6 +85,17 @@ SMALL = [
     ("e512_g1_T77_d1000", wl.GateConfig(512, 1, 1, 8, 2.827), 77, 1000),
     ("e512_g16_fused32_T9000_d264", wl.GateConfig(512, 16, 4, 8, 2.5), 9000, 264),
     ("e512_g64_fused32_T16500_d96", wl.GateConfig(512, 64, 8, 6, 1.0), 16500, 96),
+    # expert counts that are odd multiples of 64: the float32 GEMM pads the
+    # last expert tile to 128 (zero rows, dropped columns); split and fused
+    # tiles of both heights
+    ("e64_g4_T300_d1024", wl.GateConfig(64, 4, 2, 6, 1.0), 300, 1024),
+    ("e192_g8_T100_d7168", wl.GateConfig(192, 8, 4, 8, 2.5), 100, 7168),
+    ("e320_g1_T40_d7168", wl.GateConfig(320, 1, 1, 8, 2.827), 40, 7168),
+    ("e448_g8_T77_d4096", wl.GateConfig(448, 8, 4, 8, 1.0), 77, 4096),
+    ("e64_g1_fused_T8200_d128", wl.GateConfig(64, 1, 1, 8, 1.0), 8200, 128),
+    ("e192_g8_fused64_T16384_d256", wl.GateConfig(192, 8, 4, 8, 2.5), 16384, 256),
+    ("e320_g4_fused32_T16389_d200", wl.GateConfig(320, 4, 2, 8, 2.5), 16389, 200),
+    ("e448_g8_fused32_T9000_d264", wl.GateConfig(448, 8, 4, 8, 2.5), 9000, 264),
 ]
 
 
@@ -127,14 +138,15 @@ def test_gate_parity_small(o, name, gc, T, d, order):
 # multiple of 8, ragged last token tiles; and both fused tile heights.
 PLAN_SWEEP = [(2, 256), (33, 384), (65, 256), (129, 384), (300, 256), (511, 384),
               (1000, 256), (2047, 384), (4000, 256), (6000, 384), (8191, 256), (12000, 384),
-              (20000, 384), (256, 512), (3000, 512), (10000, 512)]
+              (20000, 384), (256, 512), (3000, 512), (10000, 512), (300, 192), (5000, 448)]
 
 
 @pytest.mark.parametrize("T,E", PLAN_SWEEP, ids=[f"T{t}_E{e}" for t, e in PLAN_SWEEP])
 def test_gate_plan_sweep(o, T, E):
     """Full-width d over the batch sizes where the GEMM plan changes; the
     oracle on sampled tokens (first, last and random), properties on all."""
-    gc = {256: wl.DSV3, 384: wl.KIMI_K2, 512: wl.GateConfig(512, 8, 4, 8, 2.5)}[E]
+    gc = {256: wl.DSV3, 384: wl.KIMI_K2, 512: wl.GateConfig(512, 8, 4, 8, 2.5),
+          192: wl.GateConfig(192, 8, 4, 8, 2.5), 448: wl.GateConfig(448, 8, 4, 8, 2.5)}[E]
     d = 7168
     say(f"[plan] T={T} E={E}")
     gi = wl.make_gate_inputs(T, d, gc, seed=T * 7 + E)
@@ -158,7 +170,9 @@ def test_gate_plan_sweep(o, T, E):
     # full d with blocked summation: fused 64- and 32-token tiles flushing
     # every 16 chunks, and split tiles with long k-slices (1 and 5 slices)
     (16384, 384, 7168), (20480, 256, 7168), (4096, 256, 7168), (512, 384, 7168),
-    (9000, 512, 7168), (256, 512, 7168)])
+    (9000, 512, 7168), (256, 512, 7168),
+    # padded expert tiles (E an odd multiple of 64): split and fused
+    (300, 192, 7168), (9000, 448, 1024), (16384, 320, 512), (100, 64, 2048)])
 def test_logits_exact_on_integer_inputs(o, T, E, d):
     """x small integers, W integers times 2^-8: every partial sum is exact in
     float32, so GPU logits equal the oracle's bit for bit on both the split

@@ -21,7 +21,8 @@ CHILD = textwrap.dedent("""
     from sigmoid_group_limited_amd import workloads as wl
     o = oracle.Oracle(LIB)
     for gc, T, d in [(wl.DSV3, 37, 64), (wl.KIMI_K2, 20, 40), (wl.GateConfig(128, 64, 4, 8, 1.0), 9, 24),
-                     (wl.DSV3, 1, 8), (wl.GateConfig(512, 8, 4, 8, 2.5), 5, 16)]:
+                     (wl.DSV3, 1, 8), (wl.GateConfig(512, 8, 4, 8, 2.5), 5, 16),
+                     (wl.GateConfig(192, 8, 4, 8, 2.5), 11, 24), (wl.GateConfig(64, 4, 2, 6, 1.0), 7, 8)]:
         gi = wl.make_gate_inputs(T, d, gc, seed=T)
         for opts in ({}, {"score_func": 1}, {"mask_zero": 1, "denom_eps": 1e-20}, {"renorm": 2}):
             for bias in (gi.bias, None):
