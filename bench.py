@@ -371,6 +371,56 @@ def decode_line(name: str, calls: int = 20, replays: int = 5, logits_path: int =
             "graph_replay_matches_eager": bool(same)}
 
 
+def gate_sweep():
+    """Gate time per call across batch sizes, both logits routes, for the
+    DeepSeek-V3 (E=256) and Kimi-K2 (E=384) gates at d=7168: graph-replayed
+    back-to-back calls on seeded synthetic inputs; one JSON line each."""
+    import torch
+
+    import sigmoid_group_limited_amd as sg
+    from sigmoid_group_limited_amd import workloads as wl
+    d = 7168
+    for gc in (wl.DSV3, wl.KIMI_K2):
+        for T in (1, 16, 64, 128, 256, 512, 1024, 2048, 4096, 8192, 16384):
+            gi = wl.make_gate_inputs(T, d, gc, seed=T)
+            x = torch.from_numpy(gi.x.view(np.int16)).cuda().view(torch.bfloat16)
+            W = torch.from_numpy(gi.W).cuda()
+            b = torch.from_numpy(gi.bias).cuda()
+            w = torch.empty((T, gc.top_k), dtype=torch.float32, device="cuda")
+            i = torch.empty((T, gc.top_k), dtype=torch.int32, device="cuda")
+            calls = 20 if T <= 1024 else 4
+            for lp in (0, 1):
+                cfg = sg.Cfg(T, d, gc.n_experts, gc.n_group, gc.topk_group, gc.top_k,
+                             gc.route_scale, logits_path=lp)
+                ws = sg.workspace(cfg)
+
+                def fn():
+                    sg.siggate_forward(x, W, b, cfg, w, i, ws)
+                fn()
+                s = torch.cuda.Stream()
+                with torch.cuda.stream(s):
+                    g = torch.cuda.CUDAGraph()
+                    with torch.cuda.graph(g, stream=s):
+                        for _ in range(calls):
+                            fn()
+                torch.cuda.synchronize()
+                g.replay()
+                torch.cuda.synchronize()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for _ in range(5):
+                    g.replay()
+                e1.record()
+                torch.cuda.synchronize()
+                us = e0.elapsed_time(e1) * 1e3 / (5 * calls)
+                flops = 2.0 * T * d * gc.n_experts
+                print(json.dumps({"gate_sweep": True, "E": gc.n_experts, "T": T, "logits_path": lp,
+                                  "gate_us": round(us, 2), "tokens_per_s": T / (us * 1e-6),
+                                  "fp32_tflops_equivalent": flops / (us * 1e-6) / 1e12,
+                                  "fp32_mfma_frac": flops / (us * 1e-6) / 1e12 / PEAK_FP32_MFMA_TFLOPS}),
+                      flush=True)
+
+
 def skewed_line(logits_path: int, steps: int, warmup: int) -> dict:
     """The skewed DeepSeek-V3 batch: T=65536 with 16 hot experts (two per
     group) that draw half of the 524288 pairs.  Whole steps as for the main
@@ -493,6 +543,8 @@ def main():
                          "1 the bfloat16 three-way route (then its roofline is bf16)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (counter calibration)")
+    ap.add_argument("--gate-sweep", action="store_true",
+                    help="only time the gate per call across batch sizes (both routes)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -515,6 +567,10 @@ def main():
             b.copy_(a)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes": n, "launches": 3}))
+        return
+
+    if args.gate_sweep:
+        gate_sweep()
         return
 
     lp = args.logits_path

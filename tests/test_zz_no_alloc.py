@@ -45,7 +45,9 @@ def _noalloc_c_abi(x, W, b, cfg):
 
 # (model, first T, second smaller T, logits route)
 CASES = [(wl.KIMI_K2, 256, 64, 0), (wl.DSV3, 4096, 100, 0), (wl.KIMI_K2, 16384, 256, 0),
-         (wl.DSV3, 2048, 33, 1), (wl.KIMI_K2, 256, 7, 1)]
+         (wl.DSV3, 2048, 33, 1), (wl.KIMI_K2, 256, 7, 1),
+         # 192 experts: float32 partial rows padded to whole 128-expert tiles
+         (wl.GateConfig(192, 8, 4, 8, 2.5), 300, 40, 0)]
 
 
 @pytest.mark.parametrize("gc,T1,T2,lp", CASES,
