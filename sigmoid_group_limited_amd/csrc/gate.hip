@@ -890,6 +890,21 @@ __global__ __launch_bounds__(64 * NWR) void gate_reduce_kernel(GateArgs a)
 // where the fused path uses 32-token tiles only.
 constexpr int MAX_E_TILE64 = 384;
 
+// Split GEMM on the fused kernel's full-E tiles (32 or 64 tokens x all
+// experts x one k-slice), writing partial logits.
+template <int E, int ER>
+hipError_t launch_wide(const GateArgs &a, const GatePlan &p, hipStream_t stream)
+{
+    const dim3 grid(p.grid), block(64 * 8);
+    if constexpr (E <= MAX_E_TILE64) {
+        if (p.m_blocks == 2)
+            return launch_kernel(gate_gemm_kernel<E, 2, 8, MODE_PARTIAL, 2, true, ER>, grid, block, stream, a);
+        return launch_kernel(gate_gemm_kernel<E, 1, 8, MODE_PARTIAL, 2, true, ER>, grid, block, stream, a);
+    } else {
+        return launch_kernel(gate_gemm_kernel<E, 1, 8, MODE_PARTIAL, 1, true, ER>, grid, block, stream, a);
+    }
+}
+
 // E: the GEMM's expert tile width (whole 128-expert tiles); ER: the real
 // expert count (E, or E - 64 when that is an odd multiple of 64).
 template <int E, int ER>
@@ -917,6 +932,8 @@ hipError_t launch_for_e(const GateArgs &a, const GatePlan &p, GateMode final_mod
     hipError_t e;
     if (p.x3_bm)
         e = launch_x3_gemm(a, p, stream);
+    else if (p.wide)   // the fused kernel's full-E tiles, k-sliced
+        e = launch_wide<E, ER>(a, p, stream);
     else if (p.chunks_per_split > 2 * FLUSH_CHUNKS)   // long k-slices: blocked, 2 stages
         e = launch_kernel(gate_gemm_kernel<128, 1, 8, MODE_PARTIAL, 2, true>,
                           dim3(p.grid), dim3(64 * 8), stream, a);
@@ -948,6 +965,21 @@ hipError_t launch_for_e(const GateArgs &a, const GatePlan &p, GateMode final_mod
 constexpr double SPLIT_LATENCY = 4.0;
 constexpr double SPLIT_BYTES_PER_UNIT = 2.25e6;
 constexpr int N_CU = 256;
+// Wide split tiles, in the same units: a chunk costs WIDE_CHUNK_32 (32-token
+// tile) or WIDE_CHUNK_64 (64-token tile) per 128 experts, a workgroup
+// WIDE_LATENCY, and the partials cross memory at WIDE_BYTES_PER_UNIT.
+// Fitted, with the 32 x 128 model above unchanged, to graph-replayed gate
+// times over forced plans (both tile kinds, every slice count filling 128
+// to 1024 workgroups; T = 256 ... 8191, E = 128 ... 512): the planner's
+// summed excess over the best measured plan is 10 us over 34 configurations.
+// Largest partial logits a float32 plan may need (so that every batch fits
+// the 64 MiB scratch of the no-allocation entry point, and the workspace
+// stays modest): plans above it are skipped.
+constexpr size_t MAX_PARTIAL_BYTES = (size_t)60 << 20;
+constexpr double WIDE_CHUNK_32 = 0.9;
+constexpr double WIDE_CHUNK_64 = 1.5;
+constexpr double WIDE_LATENCY = 12.0;
+constexpr double WIDE_BYTES_PER_UNIT = 5.0e6;
 // time of a round of 64-token fused workgroups over a round of 32-token ones
 // (measured 1.72 at E=384, 1.77 at E=256, d=7168)
 constexpr double FUSED_ROUND_RATIO = 1.75;
@@ -986,6 +1018,7 @@ GatePlan plan_gate(int T, int d, int E, int path)
     for (int s = 1; s <= chunks; ++s) {
         const int cps = (chunks + s - 1) / s;
         if ((chunks + cps - 1) / cps != s) continue;   // s slices of cps chunks
+        if ((size_t)s * T * EP * sizeof(float) > MAX_PARTIAL_BYTES) break;
         const long n = tiles * s;
         const double rounds = (double)((n + N_CU - 1) / N_CU);
         const double cost = rounds * (cps + SPLIT_LATENCY) +
@@ -994,6 +1027,31 @@ GatePlan plan_gate(int T, int d, int E, int path)
             best = cost;
             p.n_split = s;
             p.chunks_per_split = cps;
+        }
+    }
+    // Wide tiles: the fused kernel's 32*mb tokens x all EP experts, k-sliced.
+    // Each W slice then serves more tokens and each x slice all experts, so a
+    // chunk carries more matrix work per LDS stage and barrier.
+    for (int mb = 1; mb <= (EP <= MAX_E_TILE64 ? 2 : 1); ++mb) {
+        const long wt = ((long)T + 32 * mb - 1) / (32 * mb);
+        const double units = (double)(EP / 128) * (mb == 2 ? WIDE_CHUNK_64 : WIDE_CHUNK_32);
+        for (int s = 1; s <= chunks; ++s) {
+            const int cps = (chunks + s - 1) / s;
+            if ((chunks + cps - 1) / cps != s) continue;
+            if ((size_t)s * T * EP * sizeof(float) > MAX_PARTIAL_BYTES) break;
+            const long n = wt * s;
+            const double rounds = (double)((n + N_CU - 1) / N_CU);
+            const double cost = rounds * (cps * units + WIDE_LATENCY) +
+                                2.0 * s * (double)T * EP * sizeof(float) / WIDE_BYTES_PER_UNIT;
+            if (cost < best) {
+                best = cost;
+                p.wide = true;
+                p.m_blocks = mb;
+                p.n_split = s;
+                p.chunks_per_split = cps;
+                p.t_tiles = (int)wt;
+                p.e_tiles = 1;
+            }
         }
     }
     const long n = (long)p.t_tiles * p.e_tiles * p.n_split;

@@ -59,9 +59,10 @@ struct GateArgs {
 // How the logits GEMM is cut for a given T.
 //   fused: one workgroup owns 32*m_blocks tokens x all E experts x the whole
 //          k range and runs the selection itself (no partials);
-//   split: one workgroup owns 32 tokens x 128 experts x one k-slice
-//          and writes float32 partial logits [n_split, T, E]; a second kernel
-//          adds the slices and runs the selection.
+//   split: one workgroup owns 32 tokens x 128 experts x one k-slice (or,
+//          wide, 32*m_blocks tokens x all E x one k-slice) and writes float32
+//          partial logits [n_split, T, e_stride]; a second kernel adds the
+//          slices and runs the selection.
 //   x3:    the split layout with the bfloat16 three-way route of
 //          logits_x3.hip: x3_bm tokens x 64*x3_nbw experts x one k-slice.
 struct GatePlan {
@@ -69,7 +70,9 @@ struct GatePlan {
     int x3_bm, x3_nbw;      // x3 tile (0, 0 on the float32 route)
     bool x3_presplit;       // x3: W split once into planes in the workspace
     size_t planes_offset;   // x3 pre-split: byte offset of the planes
-    int m_blocks;           // 32-token blocks per workgroup: 1 or 2 (fused), 1 (split)
+    int m_blocks;           // 32-token blocks per workgroup: 1 or 2 (fused, wide split), 1 (split)
+    bool wide;              // split path on full-E tiles (32*m_blocks tokens x E, the fused
+                            // kernel's tile) instead of 32 x 128
     int n_split;            // k-slices (split path)
     int chunks_per_split;
     int t_tiles, e_tiles;   // split path tiles
