@@ -17,6 +17,13 @@ on the launch stream over the timed steps, against the fp32 MFMA peak.
 WRITE_SIZE, scaled by a plain-copy calibration) when that file was taken
 from the current gate kernel source, else null.
 
+Every timed section first runs its own work back to back for ``settle_ms``
+(default 200 ms) before its warm-up: after idle, the GPU's clocks take tens
+of milliseconds of load to settle (the Kimi-K2 prefill gate runs about 15%
+slower over its first 15 ms), so the timed steps see the sustained clocks
+that a continuously loaded serving or training loop runs at.  The JSON line
+gives ``settle_ms`` and the main section's ``settle_steps``.
+
 ``stages`` also carries the medians of the per-step event times, and
 ``cold`` the medians of steps that each follow a 1 GiB scrub write (x and W
 then come from HBM, not the 256 MB Infinity Cache).
@@ -74,10 +81,30 @@ PEAK_HBM_GBS = 8000.0           # MI355X HBM3E peak
 PEAK_BF16_MFMA_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
 GATE_SOURCE = os.path.join(ROOT, "sigmoid_group_limited_amd", "csrc", "gate.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gate_traffic.json")
+# wall time each timed section runs its work before its warm-up (--settle-ms)
+SETTLE_MS = 200.0
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def settle(fn, ms: float | None = None) -> int:
+    """Runs ``fn`` (which enqueues GPU work) back to back, four calls between
+    device synchronisations, until ``ms`` (default SETTLE_MS) milliseconds of
+    wall time have passed, so that the GPU's clocks have settled under load.
+    Returns the number of calls."""
+    import torch
+    ms = SETTLE_MS if ms is None else ms
+    n = 0
+    t_end = time.perf_counter() + ms * 1e-3
+    torch.cuda.synchronize()
+    while time.perf_counter() < t_end:
+        for _ in range(4):
+            fn()
+        n += 4
+        torch.cuda.synchronize()
+    return n
 
 
 def source_sha(path: str) -> str:
@@ -140,8 +167,10 @@ class Case:
     def run(self, steps: int, warmup: int):
         """Times ``steps`` whole steps (wall clock between two device
         synchronisations) and, inside the same region, each stage with HIP
-        events recorded on the launch stream."""
+        events recorded on the launch stream; before the ``warmup`` steps,
+        whole steps run for the settle time."""
         import torch
+        self.settle_steps = settle(lambda: (self.forward(), self.dispatch()))
         for _ in range(warmup):
             self.forward()
             self.dispatch()
@@ -278,6 +307,8 @@ def overlap_line(name: str, steps: int, warmup: int):
                 c.dispatch()
                 disp_done[i].record(disp_s)
 
+    # a run's batches are ordered among themselves only: synchronise after each
+    settle(lambda: (run(8), torch.cuda.synchronize()))
     run(warmup)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -340,8 +371,7 @@ def decode_line(name: str, calls: int = 20, replays: int = 5, logits_path: int =
                 for _ in range(calls):
                     fn()
         torch.cuda.synchronize()
-        g.replay()
-        torch.cuda.synchronize()
+        settle(g.replay)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for _ in range(replays):
@@ -404,8 +434,7 @@ def gate_sweep():
                         for _ in range(calls):
                             fn()
                 torch.cuda.synchronize()
-                g.replay()
-                torch.cuda.synchronize()
+                settle(g.replay)
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 e0.record()
                 for _ in range(5):
@@ -522,6 +551,7 @@ def cpu_baseline(case: Case, budget_s: float = 12.0):
 
 
 def main():
+    global SETTLE_MS
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
@@ -543,9 +573,12 @@ def main():
                          "1 the bfloat16 three-way route (then its roofline is bf16)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (counter calibration)")
+    ap.add_argument("--settle-ms", type=float, default=SETTLE_MS,
+                    help="wall time each timed section runs its work before its warm-up")
     ap.add_argument("--gate-sweep", action="store_true",
                     help="only time the gate per call across batch sizes (both routes)")
     args = ap.parse_args()
+    SETTLE_MS = args.settle_ms
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this path runs on a single MI355X "
@@ -590,6 +623,8 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_ms": SETTLE_MS,
+        "settle_steps": case.settle_steps,
         "ms_per_step": ms,
         "higher_is_better": True,
         "scaling": "weak",

@@ -106,8 +106,8 @@ typedef enum siggate_status {
                                    more than SIGGATE_SCRATCH_BYTES of workspace     */
 } siggate_status_t;
 
-/* Size of the static device scratch of siggate_forward_noalloc: 64 MiB. */
-#define SIGGATE_SCRATCH_BYTES ((size_t)64 << 20)
+/* Size of the static device scratch of siggate_forward_noalloc: 128 MiB. */
+#define SIGGATE_SCRATCH_BYTES ((size_t)128 << 20)
 
 /* Bytes of device workspace that siggate_forward and siggate_dispatch need
  * for this configuration: the larger of the two needs, counting only a call
@@ -148,8 +148,8 @@ siggate_status_t siggate_forward(const void *x, const float *W, const float *bia
  *     race and give undefined results; calls on one stream are ordered.
  *   - Configurations whose gate workspace exceeds SIGGATE_SCRATCH_BYTES
  *     return SIGGATE_ESCRATCH before anything is enqueued.  At d = 7168
- *     every T fits on logits_path 0; on logits_path 1 every T <= 10880
- *     (E = 384) or <= 16384 (E = 256) fits, and larger batches fit or not
+ *     every T fits on logits_path 0; on logits_path 1 every T <= 38314
+ *     (E = 384) or <= 65536 (E = 256) fits, and larger batches fit or not
  *     by the plan's slice count (siggate_workspace_bytes tells).
  *   - The first call on a device looks up the scratch's device address
  *     (hipGetSymbolAddress); it calls no hipMalloc or hipFree, then or ever.

@@ -23,7 +23,7 @@ SIGGATE_EUNSUPPORTED = -2
 SIGGATE_EWORKSPACE = -3
 SIGGATE_EHIP = -4
 SIGGATE_ESCRATCH = -5
-SIGGATE_SCRATCH_BYTES = 64 << 20
+SIGGATE_SCRATCH_BYTES = 128 << 20
 
 # Symbols declared in include/siggate.h
 EXPORTS = ("siggate_workspace_bytes", "siggate_forward", "siggate_forward_noalloc",

@@ -965,24 +965,25 @@ hipError_t launch_for_e(const GateArgs &a, const GatePlan &p, GateMode final_mod
 constexpr double SPLIT_LATENCY = 4.0;
 constexpr double SPLIT_BYTES_PER_UNIT = 2.25e6;
 constexpr int N_CU = 256;
-// Wide split tiles, in the same units: a chunk costs WIDE_CHUNK_32 (32-token
-// tile) or WIDE_CHUNK_64 (64-token tile) per 128 experts, a workgroup
-// WIDE_LATENCY, and the partials cross memory at WIDE_BYTES_PER_UNIT.
-// Fitted, with the 32 x 128 model above unchanged, to graph-replayed gate
-// times over forced plans (both tile kinds, every slice count filling 128
-// to 1024 workgroups; T = 256 ... 8191, E = 128 ... 512): the planner's
-// summed excess over the best measured plan is 10 us over 34 configurations.
-// Largest partial logits a float32 plan may need (so that every batch fits
-// the 64 MiB scratch of the no-allocation entry point, and the workspace
-// stays modest): plans above it are skipped.
-constexpr size_t MAX_PARTIAL_BYTES = (size_t)60 << 20;
+// Wide and fused tiles, in the same units: a chunk costs WIDE_CHUNK_32
+// (32-token tile) or WIDE_CHUNK_64 (64-token tile) per 128 experts, a
+// workgroup WIDE_LATENCY, and the partials cross memory at
+// WIDE_BYTES_PER_UNIT; a split plan (either tile kind) also pays
+// REDUCE_LAUNCH for its reduction kernel, which the fused tiles (whole k,
+// selection in the epilogue) do not need.  Fitted, with the 32 x 128 model
+// above unchanged, to graph-replayed gate times over forced plans (every
+// tile kind and slice count filling 128 to 1024 workgroups, and both fused
+// heights; T = 256 ... 24576, E = 128 ... 512): the planner's summed excess
+// over the best measured plan is about 40 us over 44 configurations.
 constexpr double WIDE_CHUNK_32 = 0.9;
 constexpr double WIDE_CHUNK_64 = 1.5;
 constexpr double WIDE_LATENCY = 12.0;
 constexpr double WIDE_BYTES_PER_UNIT = 5.0e6;
-// time of a round of 64-token fused workgroups over a round of 32-token ones
-// (measured 1.72 at E=384, 1.77 at E=256, d=7168)
-constexpr double FUSED_ROUND_RATIO = 1.75;
+constexpr double REDUCE_LAUNCH = 10.0;
+// Largest partial logits a float32 plan may need (so that every batch fits
+// the 128 MiB scratch of the no-allocation entry point, and the workspace
+// stays modest): plans above it are skipped.
+constexpr size_t MAX_PARTIAL_BYTES = (size_t)120 << 20;
 
 GatePlan plan_gate(int T, int d, int E, int path)
 {
@@ -992,29 +993,29 @@ GatePlan plan_gate(int T, int d, int E, int path)
     const int EP = (E + 127) / 128 * 128;
     p.e_stride = EP;
     const int chunks = (d + KC - 1) / KC;
-    const long tiles64 = ((long)T + 63) / 64;
     const long tiles32 = ((long)T + 31) / 32;
+    const int max_mb = EP <= MAX_E_TILE64 ? 2 : 1;
     p.n_split = 1;
     p.chunks_per_split = chunks;
     p.e_tiles = 1;
-    // Enough 64- or 32-token workgroups for every compute unit: one
-    // workgroup per token tile, all experts, whole k range, fused selection.
-    // The tile height goes by whole rounds of N_CU workgroups: a round of
-    // 64-token tiles takes about FUSED_ROUND_RATIO times a round of 32-token
-    // ones, and a partly filled last round costs a whole one.
-    if (tiles64 >= N_CU || tiles32 >= N_CU) {
-        const long r64 = (tiles64 + N_CU - 1) / N_CU, r32 = (tiles32 + N_CU - 1) / N_CU;
-        p.m_blocks = EP <= MAX_E_TILE64 && (double)r64 * FUSED_ROUND_RATIO < (double)r32 ? 2 : 1;
-        p.t_tiles = (int)(p.m_blocks == 2 ? tiles64 : tiles32);
-        p.grid = p.t_tiles;
-        return p;
-    }
-    p.split = true;
-    p.m_blocks = 1;
-    p.t_tiles = (int)tiles32;
-    p.e_tiles = EP / 128;
-    const long tiles = tiles32 * p.e_tiles;
     double best = 1e300;
+    // Fused tiles: one workgroup per 32- or 64-token tile, all experts,
+    // whole k range, selection in the epilogue.  They win once the tiles
+    // fill whole rounds of N_CU workgroups; a partly filled last round costs
+    // a whole one, which a k-split of the same tiles can avoid.
+    for (int mb = 1; mb <= max_mb; ++mb) {
+        const long wt = ((long)T + 32 * mb - 1) / (32 * mb);
+        const double units = (double)(EP / 128) * (mb == 2 ? WIDE_CHUNK_64 : WIDE_CHUNK_32);
+        const double cost = (double)((wt + N_CU - 1) / N_CU) * (chunks * units + WIDE_LATENCY);
+        if (cost < best) {
+            best = cost;
+            p.m_blocks = mb;
+            p.t_tiles = (int)wt;
+        }
+    }
+    // Split GEMM on 32-token x 128-expert tiles
+    const long tiles = tiles32 * (EP / 128);
+    int split_s = 0, split_cps = 0;
     for (int s = 1; s <= chunks; ++s) {
         const int cps = (chunks + s - 1) / s;
         if ((chunks + cps - 1) / cps != s) continue;   // s slices of cps chunks
@@ -1022,17 +1023,26 @@ GatePlan plan_gate(int T, int d, int E, int path)
         const long n = tiles * s;
         const double rounds = (double)((n + N_CU - 1) / N_CU);
         const double cost = rounds * (cps + SPLIT_LATENCY) +
-                            2.0 * s * (double)T * EP * sizeof(float) / SPLIT_BYTES_PER_UNIT;
+                            2.0 * s * (double)T * EP * sizeof(float) / SPLIT_BYTES_PER_UNIT +
+                            REDUCE_LAUNCH;
         if (cost < best) {
             best = cost;
-            p.n_split = s;
-            p.chunks_per_split = cps;
+            split_s = s;
+            split_cps = cps;
         }
+    }
+    if (split_s) {
+        p.split = true;
+        p.m_blocks = 1;
+        p.t_tiles = (int)tiles32;
+        p.e_tiles = EP / 128;
+        p.n_split = split_s;
+        p.chunks_per_split = split_cps;
     }
     // Wide tiles: the fused kernel's 32*mb tokens x all EP experts, k-sliced.
     // Each W slice then serves more tokens and each x slice all experts, so a
     // chunk carries more matrix work per LDS stage and barrier.
-    for (int mb = 1; mb <= (EP <= MAX_E_TILE64 ? 2 : 1); ++mb) {
+    for (int mb = 1; mb <= max_mb; ++mb) {
         const long wt = ((long)T + 32 * mb - 1) / (32 * mb);
         const double units = (double)(EP / 128) * (mb == 2 ? WIDE_CHUNK_64 : WIDE_CHUNK_32);
         for (int s = 1; s <= chunks; ++s) {
@@ -1042,9 +1052,11 @@ GatePlan plan_gate(int T, int d, int E, int path)
             const long n = wt * s;
             const double rounds = (double)((n + N_CU - 1) / N_CU);
             const double cost = rounds * (cps * units + WIDE_LATENCY) +
-                                2.0 * s * (double)T * EP * sizeof(float) / WIDE_BYTES_PER_UNIT;
+                                2.0 * s * (double)T * EP * sizeof(float) / WIDE_BYTES_PER_UNIT +
+                                REDUCE_LAUNCH;
             if (cost < best) {
                 best = cost;
+                p.split = true;
                 p.wide = true;
                 p.m_blocks = mb;
                 p.n_split = s;
@@ -1053,6 +1065,10 @@ GatePlan plan_gate(int T, int d, int E, int path)
                 p.e_tiles = 1;
             }
         }
+    }
+    if (!p.split) {
+        p.grid = p.t_tiles;
+        return p;
     }
     const long n = (long)p.t_tiles * p.e_tiles * p.n_split;
     p.grid = (int)((n + 7) / 8 * 8);

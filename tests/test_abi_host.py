@@ -146,7 +146,7 @@ def test_noalloc_rejects_beyond_scratch():
     enqueued: an unsupported shape, then a workspace need above the scratch."""
     assert call_noalloc(sg.Cfg(**(DSV3.__dict__ | dict(E=640, n_group=8)))) == \
         binding.SIGGATE_EUNSUPPORTED
-    big = dataclasses.replace(KIMI.with_T(65536), logits_path=1)
+    big = dataclasses.replace(KIMI.with_T(131072), logits_path=1)
     assert sg.siggate_workspace_bytes(big) > binding.SIGGATE_SCRATCH_BYTES
     assert call_noalloc(big) == binding.SIGGATE_ESCRATCH
     # every batch of the float32 route fits

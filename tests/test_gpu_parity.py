@@ -96,6 +96,10 @@ SMALL = [
     ("e192_g8_fused64_T16384_d256", wl.GateConfig(192, 8, 4, 8, 2.5), 16384, 256),
     ("e320_g4_fused32_T16389_d200", wl.GateConfig(320, 4, 2, 8, 2.5), 16389, 200),
     ("e448_g8_fused32_T9000_d264", wl.GateConfig(448, 8, 4, 8, 2.5), 9000, 264),
+    # mid-size batches on the k-sliced full-E tiles, padded expert counts:
+    # 64-token tiles (E=320, 8 slices) and 32-token ones (E=448, 3 slices)
+    ("e320_g4_wide64_T2000_d2048", wl.GateConfig(320, 4, 2, 8, 2.5), 2000, 2048),
+    ("e448_g8_wide32_T2500_d1024", wl.GateConfig(448, 8, 4, 8, 2.5), 2500, 1024),
 ]
 
 
@@ -138,7 +142,8 @@ def test_gate_parity_small(o, name, gc, T, d, order):
 # multiple of 8, ragged last token tiles; and both fused tile heights.
 PLAN_SWEEP = [(2, 256), (33, 384), (65, 256), (129, 384), (300, 256), (511, 384),
               (1000, 256), (2047, 384), (4000, 256), (6000, 384), (8191, 256), (12000, 384),
-              (20000, 384), (256, 512), (3000, 512), (10000, 512), (300, 192), (5000, 448)]
+              (20000, 384), (256, 512), (3000, 512), (10000, 512), (300, 192), (5000, 448),
+              (3000, 192)]
 
 
 @pytest.mark.parametrize("T,E", PLAN_SWEEP, ids=[f"T{t}_E{e}" for t, e in PLAN_SWEEP])
@@ -172,7 +177,10 @@ def test_gate_plan_sweep(o, T, E):
     (16384, 384, 7168), (20480, 256, 7168), (4096, 256, 7168), (512, 384, 7168),
     (9000, 512, 7168), (256, 512, 7168),
     # padded expert tiles (E an odd multiple of 64): split and fused
-    (300, 192, 7168), (9000, 448, 1024), (16384, 320, 512), (100, 64, 2048)])
+    (300, 192, 7168), (9000, 448, 1024), (16384, 320, 512), (100, 64, 2048),
+    # padded, on k-sliced full-E tiles: 32-token (E=320, 4 slices) and
+    # 64-token (E=64, 10 slices)
+    (2000, 320, 1024), (1500, 64, 7168)])
 def test_logits_exact_on_integer_inputs(o, T, E, d):
     """x small integers, W integers times 2^-8: every partial sum is exact in
     float32, so GPU logits equal the oracle's bit for bit on both the split

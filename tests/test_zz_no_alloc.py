@@ -91,7 +91,7 @@ def test_noalloc_rejects_beyond_scratch():
     """A configuration whose workspace exceeds the scratch is rejected before
     anything is enqueued, with its own status."""
     gc = wl.KIMI_K2
-    cfg = sg.Cfg(65536, 7168, gc.n_experts, gc.n_group, gc.topk_group, gc.top_k,
+    cfg = sg.Cfg(131072, 7168, gc.n_experts, gc.n_group, gc.topk_group, gc.top_k,
                  gc.route_scale, logits_path=1)
     assert sg.siggate_workspace_bytes(cfg) > binding.SIGGATE_SCRATCH_BYTES
     x = torch.empty((8, 7168), dtype=torch.bfloat16, device="cuda")
