@@ -450,6 +450,30 @@ def gate_sweep():
                       flush=True)
 
 
+def clock_ramp(name: str = "kimi-k2-prefill", calls: int = 400, block: int = 20):
+    """The gate's time per call after 2 s of idle: ``calls`` back-to-back
+    calls, each bracketed by HIP events on the launch stream, reported as the
+    median of each block of ``block`` calls with the elapsed time at the
+    block's end.  Shows how long the clocks take to settle under load."""
+    import torch
+    case = Case(name)
+    case.forward()
+    torch.cuda.synchronize()
+    time.sleep(2.0)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(calls + 1)]
+    ev[0].record()
+    for k in range(calls):
+        case.forward()
+        ev[k + 1].record()
+    torch.cuda.synchronize()
+    us = np.array([ev[k].elapsed_time(ev[k + 1]) * 1e3 for k in range(calls)])
+    print(json.dumps({"clock_ramp": True, "workload": name, "block_calls": block,
+                      "median_us": [round(float(np.median(us[j:j + block])), 1)
+                                    for j in range(0, calls, block)],
+                      "elapsed_ms_at_block_end": [round(float(us[:j + block].sum()) / 1e3, 1)
+                                                  for j in range(0, calls, block)]}), flush=True)
+
+
 def skewed_line(logits_path: int, steps: int, warmup: int) -> dict:
     """The skewed DeepSeek-V3 batch: T=65536 with 16 hot experts (two per
     group) that draw half of the 524288 pairs.  Whole steps as for the main
@@ -575,6 +599,8 @@ def main():
                     help="only run a plain device copy of MIB MiB (counter calibration)")
     ap.add_argument("--settle-ms", type=float, default=SETTLE_MS,
                     help="wall time each timed section runs its work before its warm-up")
+    ap.add_argument("--clock-ramp", action="store_true",
+                    help="only time 400 back-to-back gate calls after 2 s idle (clock settling)")
     ap.add_argument("--gate-sweep", action="store_true",
                     help="only time the gate per call across batch sizes (both routes)")
     args = ap.parse_args()
@@ -604,6 +630,10 @@ def main():
 
     if args.gate_sweep:
         gate_sweep()
+        return
+
+    if args.clock_ramp:
+        clock_ramp(args.workload)
         return
 
     lp = args.logits_path

@@ -65,12 +65,12 @@ SMALL = [
     ("e384_g2_T129_d264", wl.GateConfig(384, 2, 1, 8, 2.827), 129, 264),
     ("e256_g8_k3_T4100_d256", wl.GateConfig(256, 8, 4, 3, 2.5), 4100, 256),
     # fused (single k-slice) paths: 32-token and 64-token workgroups, ragged
-    # tails; the tile height goes by whole rounds of 256 workgroups, so
-    # 8180 and 16389-24576 tokens take 32-token tiles, 8229-16384 and
-    # 24577-32768 take 64-token ones (a partly filled round among them)
+    # tails, partly filled rounds of 256 workgroups; the planner costs them
+    # beside the k-split plans, and at these short rows they win
     ("dsv3_fused32_T8180_d256", wl.DSV3, 8180, 256),
     ("dsv3_fused64_partial_round_T8229_d256", wl.DSV3, 8229, 256),
-    ("kimi_fused32_T16389_d256", wl.KIMI_K2, 16389, 256),
+    ("kimi_fused32_T5000_d512", wl.KIMI_K2, 5000, 512),
+    ("kimi_fused64_two_rounds_T16389_d256", wl.KIMI_K2, 16389, 256),
     ("kimi_fused64_T16380_d256", wl.KIMI_K2, 16380, 256),
     ("dsv3_fused64_T16350_d200", wl.DSV3, 16350, 200),
     ("e128_g4_fused64_T16321_d96", wl.GateConfig(128, 4, 2, 6, 1.0), 16321, 96),
@@ -79,7 +79,7 @@ SMALL = [
     ("e128_g64_kg4_k8_all_kept_T300_d512", wl.GateConfig(128, 64, 4, 8, 1.0), 300, 512),
     # every group kept (the group stage selects nothing away)
     ("e256_g8_kg8_T200_d1024", wl.GateConfig(256, 8, 8, 8, 2.5), 200, 1024),
-    ("e128_g1_fused32_T20000_d136", wl.GateConfig(128, 1, 1, 8, 2.5), 20000, 136),
+    ("e128_g1_fused64_T20000_d136", wl.GateConfig(128, 1, 1, 8, 2.5), 20000, 136),
     # 512 experts: split tiles of 4 expert tiles, fused tiles of 32 tokens only
     ("e512_g8_T300_d7168", wl.GateConfig(512, 8, 4, 8, 2.5), 300, 7168),
     ("e512_g1_T77_d1000", wl.GateConfig(512, 1, 1, 8, 2.827), 77, 1000),
@@ -94,7 +94,8 @@ SMALL = [
     ("e448_g8_T77_d4096", wl.GateConfig(448, 8, 4, 8, 1.0), 77, 4096),
     ("e64_g1_fused_T8200_d128", wl.GateConfig(64, 1, 1, 8, 1.0), 8200, 128),
     ("e192_g8_fused64_T16384_d256", wl.GateConfig(192, 8, 4, 8, 2.5), 16384, 256),
-    ("e320_g4_fused32_T16389_d200", wl.GateConfig(320, 4, 2, 8, 2.5), 16389, 200),
+    ("e320_g4_fused64_T16389_d200", wl.GateConfig(320, 4, 2, 8, 2.5), 16389, 200),
+    ("e320_g4_fused32_T4500_d256", wl.GateConfig(320, 4, 2, 8, 2.5), 4500, 256),
     ("e448_g8_fused32_T9000_d264", wl.GateConfig(448, 8, 4, 8, 2.5), 9000, 264),
     # mid-size batches on the k-sliced full-E tiles, padded expert counts:
     # 64-token tiles (E=320, 8 slices) and 32-token ones (E=448, 3 slices)
@@ -173,9 +174,10 @@ def test_gate_plan_sweep(o, T, E):
 @pytest.mark.parametrize("T,E,d", [
     (100, 256, 7168), (16384, 384, 96), (9000, 128, 40),
     # full d with blocked summation: fused 64- and 32-token tiles flushing
-    # every 16 chunks, and split tiles with long k-slices (1 and 5 slices)
-    (16384, 384, 7168), (20480, 256, 7168), (4096, 256, 7168), (512, 384, 7168),
-    (9000, 512, 7168), (256, 512, 7168),
+    # every 16 chunks, full-E split tiles with 56-chunk slices, and 32 x 128
+    # split tiles with long k-slices (2 and 5 slices)
+    (16384, 384, 7168), (8192, 512, 7168), (20480, 256, 7168), (4096, 256, 7168),
+    (512, 384, 7168), (9000, 512, 7168), (256, 512, 7168),
     # padded expert tiles (E an odd multiple of 64): split and fused
     (300, 192, 7168), (9000, 448, 1024), (16384, 320, 512), (100, 64, 2048),
     # padded, on k-sliced full-E tiles: 32-token (E=320, 4 slices) and
