@@ -520,11 +520,12 @@ def score_error(case: Case, o, n: int, margins: np.ndarray, same: np.ndarray) ->
             "near_band_mismatch": int((band & ~same).sum())}
 
 
-def cpu_baseline(case: Case, budget_s: float = 12.0):
+def cpu_baseline(case: Case, budget_s: float = 12.0, min_total_s: float = 10.0):
     """The oracle, as it stands, on the first n tokens of the workload: gate,
     then dispatch and row gather of those tokens' pairs.  n grows from 256
     until the run takes about budget_s / 4, then one timed run at the size
-    that fits the budget."""
+    that fits the budget; when that is the whole batch and shorter than
+    min_total_s, the run is repeated until the timed runs add up to it."""
     import oracle
     o = oracle.load()
     c = case.cfg
@@ -553,6 +554,13 @@ def cpu_baseline(case: Case, budget_s: float = 12.0):
         if n_final != n:
             n = n_final
             dt = one(n)
+    runs, total = 1, dt
+    gate_total, disp_total = split["gate"], split["dispatch"]
+    while total < min_total_s:
+        total += one(n)
+        gate_total += split["gate"]
+        disp_total += split["dispatch"]
+        runs += 1
     # the same tokens on the GPU (the last timed step's outputs) against the
     # oracle run just timed, with the exemption rule of the parity tests
     r = split["result"]
@@ -566,12 +574,13 @@ def cpu_baseline(case: Case, budget_s: float = 12.0):
               "index_mismatch_nonexempt": int((~same & ~exempt).sum()),
               "weight_max_rel": float(rel.max()) if rel.size else 0.0}
     parity.update(score_error(case, o, n, r.margins, same))
-    return dict(value=n / dt, unit="tokens/s", cores=o.num_threads(), kind="oracle",
-                gate_tokens_per_s=n / split["gate"],
-                dispatch_tokens_per_s=n / split["dispatch"],
+    return dict(value=n * runs / total, unit="tokens/s", cores=o.num_threads(), kind="oracle",
+                gate_tokens_per_s=n * runs / gate_total,
+                dispatch_tokens_per_s=n * runs / disp_total,
                 gpu_parity=parity,
                 sample=f"first {n} of {case.w.T} tokens of {case.w.name}: float64 gate, "
-                       f"dispatch and row gather of their {n * c.top_k} pairs; {dt:.2f} s")
+                       f"dispatch and row gather of their {n * c.top_k} pairs; "
+                       f"{runs} timed run{'s' if runs > 1 else ''}, {total:.2f} s")
 
 
 def main():

@@ -6,6 +6,7 @@ import dataclasses
 import os
 import re
 
+import numpy as np
 import pytest
 
 import sigmoid_group_limited_amd as sg
@@ -152,6 +153,20 @@ def test_noalloc_rejects_beyond_scratch():
     # every batch of the float32 route fits
     for T in (1, 256, 4096, 6144, 8191, 65536):
         assert sg.siggate_workspace_bytes(KIMI.with_T(T)) <= binding.SIGGATE_SCRATCH_BYTES
+
+
+def test_float32_plans_fit_the_scratch():
+    """The float32 planner skips plans whose partial logits exceed 120 MiB,
+    so every batch of that route fits the no-allocation scratch, at every
+    supported expert count and row length."""
+    rng = np.random.default_rng(7)
+    Ts = sorted(set([1, 2, 255, 256, 257] + [int(t) for t in np.geomspace(300, 300000, 60)] +
+                    [int(t) for t in rng.integers(1, 70000, 60)]))
+    for E in range(64, 513, 64):
+        for d in (96, 1024, 7168):
+            for T in Ts:
+                c = sg.Cfg(T, d, E, 1, 1, 8, 1.0)
+                assert sg.siggate_workspace_bytes(c) <= binding.SIGGATE_SCRATCH_BYTES, (E, d, T)
 
 
 def test_scratch_size_matches_header():

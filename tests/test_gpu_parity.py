@@ -144,7 +144,11 @@ def test_gate_parity_small(o, name, gc, T, d, order):
 PLAN_SWEEP = [(2, 256), (33, 384), (65, 256), (129, 384), (300, 256), (511, 384),
               (1000, 256), (2047, 384), (4000, 256), (6000, 384), (8191, 256), (12000, 384),
               (20000, 384), (256, 512), (3000, 512), (10000, 512), (300, 192), (5000, 448),
-              (3000, 192)]
+              (3000, 192),
+              # where fused 64-token tiles start to fill whole rounds, the
+              # k-split plan just past a full round, and 32 x 128 tiles at
+              # 512 experts for large batches
+              (13633, 384), (16385, 256), (8800, 512), (33000, 512)]
 
 
 @pytest.mark.parametrize("T,E", PLAN_SWEEP, ids=[f"T{t}_E{e}" for t, e in PLAN_SWEEP])
