@@ -19,12 +19,16 @@
 //   come from LDS, which holds KC = 32 k-columns of W [E x KC] and of x
 //   [BM x KC] (x upcast from bfloat16 to float32 on the way in, exact),
 //   double-buffered, with two more chunks of global loads in flight.
-//   Small batches (fewer than 256 such workgroups) use a split GEMM
-//   instead: a workgroup owns 32 tokens x 128 experts x one slice of
-//   the k range and writes float32 partial logits; a second kernel adds the
-//   slices in a fixed order (deterministic) and runs the same selection.
-//   Split tiles are ordered so that the token tiles sharing a W slice run on
-//   one XCD (one L2), and W crosses from HBM about once.
+//   Batches whose fused tiles would leave compute units idle (all small
+//   batches, and most mid-size ones, where a partly filled last round of
+//   256 workgroups costs a whole round) split the k range instead: a
+//   workgroup owns 32 tokens x 128 experts, or the fused tile's 32*MB
+//   tokens x all experts, over one slice of k and writes float32 partial
+//   logits; a second kernel adds the slices in a fixed order
+//   (deterministic) and runs the same selection.  A cost model picks the
+//   plan (plan_gate).  Split tiles are ordered so that the token tiles
+//   sharing a W slice run on one XCD (one L2), and W crosses from HBM about
+//   once.
 #include <math.h>
 
 #include "siggate_internal.h"
