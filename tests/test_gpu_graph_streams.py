@@ -53,8 +53,9 @@ def _snapshot(bufs):
 
 
 @pytest.mark.parametrize("gc,T,d", [(wl.KIMI_K2, 256, 7168), (wl.DSV3, 64, 7168),
-                                    (wl.DSV3, 2048, 1024), (wl.KIMI_K2, 16384, 512)],
-                         ids=["kimi_T256", "dsv3_T64", "dsv3_T2048", "kimi_T16384"])
+                                    (wl.DSV3, 2048, 1024), (wl.KIMI_K2, 4096, 7168),
+                                    (wl.KIMI_K2, 16384, 512)],
+                         ids=["kimi_T256", "dsv3_T64", "dsv3_T2048", "kimi_T4096", "kimi_T16384"])
 @pytest.mark.parametrize("lp", [0, 1], ids=["fp32", "bf16x3"])
 def test_graph_replay_matches_eager(gc, T, d, lp):
     say(f"[graph] E={gc.n_experts} T={T} d={d} logits_path={lp}")
