@@ -22,7 +22,7 @@ pytestmark = pytest.mark.gpu
 
 torch = pytest.importorskip("torch")
 
-N_CASES = 24
+N_CASES = 40
 
 
 @pytest.fixture(scope="module")
@@ -42,12 +42,12 @@ def gpu():
 def draw_case(seed: int):
     """A supported configuration and its sizes, from one seed."""
     r = np.random.default_rng(1000 + seed)
-    E = int(r.choice([128, 256, 384]))
+    E = int(r.choice([64, 128, 192, 256, 320, 384, 448, 512]))
     groups = [g for g in (1, 2, 4, 8, 16, 32, 64) if E % g == 0 and E // g >= 2]
     G = int(r.choice(groups))
     KG = int(r.integers(1, G + 1))
     K = int(r.integers(1, min(8, KG * (E // G)) + 1))
-    T = int(r.choice([1, 2, 7, 63, 64, 65, 300, 511, 1000, 1023, 1024, 1500, 3000]))
+    T = int(r.choice([1, 2, 7, 63, 64, 65, 300, 511, 1000, 1023, 1024, 1500, 3000, 4100, 6000]))
     d = int(8 * r.integers(1, 257))
     opts = dict(order=int(r.integers(0, 2)), score_func=int(r.random() < 0.25),
                 renorm=int(r.choice([0, 0, 1, 2])), mask_zero=int(r.random() < 0.25),
